@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an AMD GPU (MI355X / gfx950) and the built HIP library")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The built library on a GPU.  Fails loudly (not skips) when the library is missing on a GPU machine."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from paged_kv_cache_199_amd import _lib
+
+    return _lib.load()
