@@ -1,0 +1,253 @@
+"""Benchmark: one step = the whole decode hot path on one batch: the slot-mapped append of each
+sequence's new K/V row (when the workload has one) plus paged decode attention with its split-K
+combine, all through the C ABI.
+
+    python bench.py [--steps K] [--warmup W] [--workload conc32_bf16] [--partition-size P]
+
+Prints ONE JSON line.  `value` is whole-step throughput in GB/s of algorithmic bytes (every attended
+K/V row once, Q, the output, the LSE, the block ids and lengths, plus the appended rows), with every
+input resident in HBM before the clock starts.  The K/V pool is cloned into enough copies (>= 1 GiB in
+total) that consecutive steps never hit the 256 MB Infinity Cache; step i uses copy i mod R.
+`roofline` reports the partition kernel alone, timed by HIP events the library records around it on
+the launch stream.  `cpu_baseline` times the float64 oracle on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the decode must move at least once (split-K partials excluded: they are overhead)."""
+    e = 4 if w.spec.dtype == "f32" else 2
+    KVH, D, B = w.spec.num_kv_heads, w.spec.head_dim, w.spec.block_size
+    rows_by_block = {}
+    for s in range(w.num_seqs):
+        n = int(w.context_lens[s])
+        for j in range((n + B - 1) // B):
+            blk = int(w.block_tables[s, j])
+            rows_by_block[blk] = max(rows_by_block.get(blk, 0), min(B, n - j * B))
+    kv_tokens = sum(rows_by_block.values())          # shared pages count once
+    kv = kv_tokens * KVH * D * 2 * e
+    qo = w.total_q * w.spec.num_heads * D * e * 2 + w.total_q * w.spec.num_heads * 4
+    meta = int(((w.context_lens.astype(np.int64) + B - 1) // B).sum()) * 4 + w.num_seqs * 8
+    return int(kv + qo + meta)
+
+
+def write_bytes(w) -> int:
+    if w.slot_mapping is None:
+        return 0
+    e = 4 if w.spec.dtype == "f32" else 2
+    rows = int(w.slot_mapping.shape[0])
+    return rows * w.spec.num_kv_heads * w.spec.head_dim * e * 2 * 2 + rows * 8
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_199_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, path: str):
+    """HBM bytes per launch of the partition kernel from committed rocprofv3 counter runs, or None when
+    the kernels changed since they were taken."""
+    f = os.path.join(PROFILES, f"traffic_{path}_{workload}.json")
+    if not os.path.exists(f):
+        return None
+    d = json.load(open(f))
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it is, single-threaded BLAS, on whole sequences (cycling through the workload)
+    until ~budget_s of CPU work."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_attention as O
+    import torch
+
+    def bits(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    q, kc, vc = bits(w.q), bits(w.k_cache), bits(w.v_cache)
+    B = w.spec.block_size
+    e = 4 if w.spec.dtype == "f32" else 2
+    t_used, nbytes, tokens, n_runs = 0.0, 0, 0, 0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            s = n_runs % w.num_seqs
+            t0 = time.perf_counter()
+            O.paged_decode_attention(q, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale,
+                                     w.spec.num_kv_heads, B, seqs=[s])
+            t_used += time.perf_counter() - t0
+            n = int(w.context_lens[s])
+            qs = int(w.q_lens[s])
+            nbytes += n * w.spec.num_kv_heads * w.spec.head_dim * 2 * e + qs * w.spec.num_heads * (
+                w.spec.head_dim * e * 2 + 4) + ((n + B - 1) // B) * 4 + 8
+            tokens += n
+            n_runs += 1
+    return {
+        "value": round(nbytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n_runs} sequence decodes cycling over the {w.num_seqs} sequences of the workload "
+                  f"({tokens} context tokens, all heads), numpy float64, 1 BLAS thread, {t_used:.1f} s",
+        "attended_tokens_per_s": round(tokens / t_used, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="conc32_bf16")
+    ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own, 0: policy")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
+    ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_199_amd import _lib
+    from paged_kv_cache_199_amd import workloads as W
+
+    _lib.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = 1 << 28
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 5}))
+        return
+
+    spec = W.named(args.workload)
+    P = spec.partition_size if args.partition_size < 0 else args.partition_size
+    path = {"auto": _lib.PATH_AUTO, "valu": _lib.PATH_VALU, "mfma": _lib.PATH_MFMA}[args.path]
+    w = W.build(spec, dev)
+    meta = w.device_meta(dev)
+    H, KVH, D = spec.num_heads, spec.num_kv_heads, spec.head_dim
+    pool_bytes = w.k_cache.numel() * w.k_cache.element_size() * 2
+    R = max(1, math.ceil(args.min_pool_bytes / pool_bytes))
+    kcs = [w.k_cache] + [w.k_cache.clone() for _ in range(R - 1)]
+    vcs = [w.v_cache] + [w.v_cache.clone() for _ in range(R - 1)]
+    out = torch.empty_like(w.q)
+    lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
+    code = _lib.PKV_BF16 if spec.dtype == "bf16" else _lib.PKV_F32
+    P_used = _lib.decode_partition_size(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D,
+                                        code, P, path)
+    ws_bytes = _lib.decode_workspace_bytes(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D,
+                                           code, P, path)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    q_lens = None if w.uniform_q else meta["q_lens"]
+    stream = torch.cuda.current_stream()
+    total = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for b, e in ev:           # create the underlying hipEvents so their handles can be passed down
+        b.record(stream)
+        e.record(stream)
+
+    def step(i, events=None):
+        r = i % R
+        if w.slot_mapping is not None:
+            _lib.kv_cache_write(w.new_k, w.new_v, meta["slot_mapping"], kcs[r], vcs[r])
+        _lib.paged_attn_decode(w.q, kcs[r], vcs[r], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
+                               H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
+                               partition_size=P, path=path, workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = float(np.mean([b.elapsed_time(e) for b, e in ev]))
+
+    dec_bytes = algorithmic_bytes(w)
+    step_bytes = dec_bytes + write_bytes(w)
+    tokens = int(w.context_lens.astype(np.int64).sum())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (k_ms * 1e-3) / 1e9
+    traffic = measured_traffic(spec.name, args.path)
+    res = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + attended tokens/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled 16-token pages)",
+        "config": {
+            "workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
+            "head_dim": D, "block_size": spec.block_size, "q_len": w.max_q_len,
+            "context_tokens": tokens, "max_context_len": w.max_context_len, "partition_size": P_used,
+            "path": args.path, "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": step_bytes,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_valu_kernel" if args.path != "mfma" else "decode_mfma_kernel",
+            "kernel_ms": round(k_ms, 5),
+            "algorithmic_bytes_per_launch": dec_bytes,
+        },
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+/*
+ * pkv.h — C ABI of the paged-KV decode-attention library (libpkv.so), written for AMD CDNA4 (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * The inferd page describes a paged KV cache as a block allocator plus a page table and keeps a plain
+ * paged-attention reference next to it (repository tree; its results table shows the paged path equal
+ * to the unpaged one).  The lfm25-inference page ("Runtime Design") runs paged grouped-query (GQA/XQA)
+ * decode attention with a split-K reduction, without per-step allocation, over engine-owned KV pages
+ * of 16 tokens ("Run Inference": page size 16; page size is a startup policy).  This library is that
+ * hot path: the slot-mapped append of new K/V rows into their pages, and decode attention of 1..few
+ * new query tokens per sequence over K/V gathered through the block table.
+ *
+ * For sequence s with context length ctx_s (which COUNTS its q_s new tokens, the last q_s positions),
+ * query row i in [0, q_s) and query head h:
+ *     kv head  = h / (num_heads / num_kv_heads)
+ *     visible  = key positions 0 .. ctx_s - q_s + i            (causal among the new tokens)
+ *     out      = softmax_t(scale * <q, K[t]>) . V               (fp32 accumulation)
+ *     lse      = ln sum_t exp(scale * <q, K[t]>)                (natural log, fp32)
+ *
+ * Memory layout (all arrays dense, row-major, device memory owned by the caller):
+ *     q, out         [total_q, num_heads, head_dim]        rows packed sequence after sequence
+ *     k_cache        [num_blocks, num_kv_heads, block_size, head_dim]   (token rows inside a block)
+ *     v_cache        [num_blocks, num_kv_heads, head_dim, block_size]   (dim rows inside a block)
+ *     block_tables   int32 [num_seqs, max_blocks_per_seq]  logical block j of sequence s -> physical id
+ *     context_lens   int32 [num_seqs]
+ *     q_lens         int32 [num_seqs]  or NULL: every sequence has max_q_len new tokens
+ *     lse            float [total_q, num_heads]  or NULL
+ *     slot_mapping   int64 [num_tokens]  slot = physical_block * block_size + offset; < 0 skips the row
+ * Logical token t of sequence s sits in block block_tables[s][t / block_size] at offset t % block_size.
+ *
+ * Element types: PKV_F32 (q, caches, out all fp32) or PKV_BF16 (all bf16).  head_dim is 64 or 128,
+ * block_size is 16.
+ *
+ * Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream).  They never allocate,
+ * never synchronize and never read device memory on the host.  Host-side validation happens before
+ * any launch; a non-zero return means nothing was enqueued (except PKV_ERR_LAUNCH, which reports a
+ * failed launch).  Device data is trusted to satisfy the preconditions listed per call; the kernels
+ * stay memory-safe when it does not (out-of-range block ids, slots and lengths are skipped or
+ * clamped) but the results are then unspecified.  Calls that share output or workspace buffers must
+ * not overlap on different streams.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* sizes are inconsistent (e.g. num_heads % num_kv_heads != 0) */
+  PKV_ERR_UNSUPPORTED = -3, /* head_dim, block_size, dtype or partition size outside what is built */
+  PKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than pkv_decode_workspace_bytes() */
+  PKV_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Kernel family for the partition pass.  AUTO lets the library choose. */
+typedef enum pkv_path { PKV_PATH_AUTO = 0, PKV_PATH_VALU = 1, PKV_PATH_MFMA = 2 } pkv_path;
+
+/* Optional tuning / instrumentation for pkv_paged_attn_decode.  Pass NULL for defaults; a zeroed
+ * struct also means defaults. */
+typedef struct pkv_decode_options {
+  int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy */
+  int path;                 /* pkv_path */
+  void *event_main_begin;   /* hipEvent_t recorded on `stream` right before the partition kernel */
+  void *event_main_end;     /* hipEvent_t recorded right after it (before the combine kernel) */
+} pkv_decode_options;
+
+/*
+ * Slot-mapped KV append (lfm25-inference, "Runtime Design": engine-owned KV pages; inferd follow-up
+ * plan: the block allocator feeding live decode).  For every t in [0, num_tokens) with
+ * slot_mapping[t] >= 0:
+ *     k_cache[slot / B][h][slot % B][:] = k[t][h][:]      v_cache[slot / B][h][:][slot % B] = v[t][h][:]
+ * for all kv heads h.  k, v: [num_tokens, num_kv_heads, head_dim] of `dtype`.  Bits are copied
+ * unchanged.  Slots >= num_blocks * block_size are skipped.  Preconditions: non-negative slots are
+ * unique (duplicates race); writing into a block several sequences share is the caller's
+ * copy-on-write decision.  num_tokens == 0 is a no-op.
+ */
+int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping,
+                       void *k_cache, void *v_cache,
+                       int64_t num_tokens, int64_t num_blocks,
+                       int num_kv_heads, int head_dim, int block_size,
+                       int dtype, void *stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options (0 is possible:
+ * a single-partition launch with uniform q needs none).  The split-K partials take
+ * ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes.
+ */
+size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int max_context_len,
+                                  int num_heads, int num_kv_heads, int head_dim, int dtype,
+                                  const pkv_decode_options *opts);
+
+/* The partition size the library uses for these sizes and options (options->partition_size when it
+ * is set, else the policy's choice).  Returns a negative pkv_status on bad sizes. */
+int pkv_decode_partition_size(int num_seqs, int total_q, int max_q_len, int max_context_len,
+                              int num_heads, int num_kv_heads, int head_dim, int dtype,
+                              const pkv_decode_options *opts);
+
+/*
+ * Paged decode attention (definition at the top of this file), with a split-K pass over key
+ * partitions of P tokens merged through their log-sum-exp (lfm25-inference, "Runtime Design").
+ * Preconditions on device data: 1 <= q_lens[s] <= context_lens[s] <= max_context_len,
+ * context_lens[s] <= max_blocks_per_seq * block_size, block ids in [0, num_blocks), and
+ * sum(q_lens) == total_q (q_lens == NULL: total_q == num_seqs * max_q_len).
+ * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0).
+ * `scale` multiplies the raw dot products (usually 1/sqrt(head_dim)).
+ */
+int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          const int32_t *q_lens, void *out, float *lse,
+                          int num_seqs, int max_blocks_per_seq, int total_q, int max_q_len,
+                          int max_context_len, int64_t num_blocks,
+                          int num_heads, int num_kv_heads, int head_dim, int block_size,
+                          float scale, int dtype, const pkv_decode_options *opts,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable text for a pkv_status value (static storage). */
+const char *pkv_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

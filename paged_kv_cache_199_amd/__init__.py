@@ -1,0 +1,9 @@
+"""Paged-KV decode attention for AMD MI355X (gfx950): HIP kernels behind a C ABI (include/pkv.h).
+
+    from paged_kv_cache_199_amd import kv_cache_write, paged_attn_decode
+"""
+from ._lib import (PATH_AUTO, PATH_MFMA, PATH_VALU, decode_partition_size, decode_workspace_bytes,
+                   kv_cache_write, load, paged_attn_decode)
+
+__all__ = ["kv_cache_write", "paged_attn_decode", "decode_workspace_bytes", "decode_partition_size",
+           "load", "PATH_AUTO", "PATH_VALU", "PATH_MFMA"]

@@ -1,0 +1,52 @@
+// Slot-mapped KV append: new K/V rows go to the page slots the engine assigned to them.
+// (lfm25-inference, "Runtime Design": KV pages belong to the engine; inferd follow-up plan: the
+// block allocator feeding live decode.)  Bits are moved unchanged, so the write is exact.
+//
+// One 64-thread workgroup per (new token, kv head).  K pages are token-major: the row is one
+// contiguous run, copied with 16-byte moves.  V pages are dim-major: element d of the row lands at
+// stride block_size, one element per lane.
+#include "device_common.h"
+
+namespace pkv {
+
+template <int E, int D>
+__global__ __launch_bounds__(64) void kv_write_kernel(const void *__restrict__ k, const void *__restrict__ v,
+                                                      const int64_t *__restrict__ slots,
+                                                      void *__restrict__ kc, void *__restrict__ vc,
+                                                      int64_t num_slots, int kvh_n) {
+  using elem_t = typename std::conditional<E == 2, uint16_t, uint32_t>::type;
+  constexpr int ROWB = D * E;
+  const int64_t row = blockIdx.x;            // token * kvh_n + head
+  const int64_t t = row / kvh_n;
+  const int h = (int)(row - t * kvh_n);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot - blk * kBlock);
+  const int lane = threadIdx.x;
+  const int64_t page = blk * kvh_n + h;
+  const char *ks = static_cast<const char *>(k) + row * ROWB;
+  char *kd = static_cast<char *>(kc) + (page * kBlock + off) * ROWB;
+  for (int c = lane; c < ROWB / 16; c += 64)
+    *reinterpret_cast<uint4 *>(kd + c * 16) = *reinterpret_cast<const uint4 *>(ks + c * 16);
+  const elem_t *vs = static_cast<const elem_t *>(v) + row * D;
+  elem_t *vd = static_cast<elem_t *>(vc) + page * D * kBlock + off;
+  for (int d = lane; d < D; d += 64) vd[d * kBlock] = vs[d];
+}
+
+hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,
+                           int64_t num_tokens, int64_t num_blocks, int kvh_n, int head_dim, bool bf16,
+                           hipStream_t st) {
+  const int64_t grid = num_tokens * kvh_n;
+  const int64_t nslots = num_blocks * kBlock;
+  if (bf16) {
+    if (head_dim == 64) kv_write_kernel<2, 64><<<grid, 64, 0, st>>>(k, v, slots, kc, vc, nslots, kvh_n);
+    else kv_write_kernel<2, 128><<<grid, 64, 0, st>>>(k, v, slots, kc, vc, nslots, kvh_n);
+  } else {
+    if (head_dim == 64) kv_write_kernel<4, 64><<<grid, 64, 0, st>>>(k, v, slots, kc, vc, nslots, kvh_n);
+    else kv_write_kernel<4, 128><<<grid, 64, 0, st>>>(k, v, slots, kc, vc, nslots, kvh_n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

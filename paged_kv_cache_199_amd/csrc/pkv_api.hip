@@ -1,0 +1,234 @@
+// Host side of the C ABI declared in include/pkv.h: argument validation, the split-K / kernel policy,
+// workspace carving and kernel launches.  Nothing here allocates, synchronizes or reads device memory.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_args.h"
+
+namespace pkv {
+hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,
+                           int64_t num_tokens, int64_t num_blocks, int kvh_n, int head_dim, bool bf16,
+                           hipStream_t st);
+hipError_t launch_decode_valu(const DecodeArgs &a, bool bf16, int head_dim, int rows_per_tile,
+                              hipStream_t st);
+int valu_max_rows(bool bf16);
+hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
+hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
+}  // namespace pkv
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+bool supported_dtype(int dtype) { return dtype == PKV_F32 || dtype == PKV_BF16; }
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+struct Plan {
+  int path;          // PKV_PATH_VALU / PKV_PATH_MFMA
+  int rows_per_tile;
+  int row_tiles;
+  int part_size;
+  int num_parts;
+  bool need_q_start;
+  size_t off_q_start, off_part_lse, off_part_o, bytes;
+};
+
+int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
+                 int num_kv_heads, int head_dim, int dtype, const pkv_decode_options *opts) {
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 1 || max_context_len < 1) return PKV_ERR_SHAPE;
+  if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (max_q_len > max_context_len) return PKV_ERR_SHAPE;
+  if (opts) {
+    const int P = opts->partition_size;
+    if (P < 0 || P % kBlockSize != 0) return PKV_ERR_UNSUPPORTED;
+    if (opts->path != PKV_PATH_AUTO && opts->path != PKV_PATH_VALU) return PKV_ERR_UNSUPPORTED;
+  }
+  return PKV_OK;
+}
+
+// Policy.  Rows per tile: the whole GQA group times the new tokens when it fits the kernel's
+// register budget, else tiles.  Partition size: the largest of 512/256/128/64 keys that still gives
+// about 2048 live workgroups (8 per CU) for a mean context of half the maximum, and no split at all
+// when the whole context fits one partition.
+Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
+               int num_kv_heads, int head_dim, int dtype, bool ragged_q,
+               const pkv_decode_options *opts) {
+  Plan pl{};
+  const bool bf16 = dtype == PKV_BF16;
+  const int G = num_heads / num_kv_heads;
+  const int rows = G * max_q_len;
+  pl.path = PKV_PATH_VALU;
+  const int rmax = pkv::valu_max_rows(bf16);
+  int R = 1;
+  while (R < rows && R < rmax) R <<= 1;
+  pl.rows_per_tile = R;
+  pl.row_tiles = ceil_div(rows, R);
+  int P = opts ? opts->partition_size : 0;
+  if (P == 0) {
+    const int64_t units1 = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
+    const int64_t mean_ctx = (max_context_len + 1) / 2;
+    P = 64;
+    for (int cand : {512, 256, 128}) {
+      if (units1 * ceil_div(mean_ctx, cand) >= 2048) {
+        P = cand;
+        break;
+      }
+    }
+  }
+  const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
+  if (P >= whole) P = whole;
+  pl.part_size = P;
+  pl.num_parts = ceil_div(max_context_len, P);
+  pl.need_q_start = ragged_q;
+  size_t off = 0;
+  pl.off_q_start = off;
+  if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
+  pl.off_part_lse = off;
+  pl.off_part_o = off;
+  if (pl.num_parts > 1) {
+    off = align_up(off + (size_t)pl.num_parts * total_q * num_heads * 4);
+    pl.off_part_o = off;
+    off = align_up(off + (size_t)pl.num_parts * total_q * num_heads * head_dim * 4);
+  }
+  pl.bytes = off;
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return (1 << 16) | 0; }
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "inconsistent sizes";
+    case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype, path or partition size";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                       void *v_cache, int64_t num_tokens, int64_t num_blocks, int num_kv_heads,
+                       int head_dim, int block_size, int dtype, void *stream) {
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || block_size != kBlockSize)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads < 1) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  if (num_tokens * num_kv_heads >= kMaxGrid) return PKV_ERR_SHAPE;
+  const hipError_t e = pkv::launch_kv_write(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_blocks,
+                                            num_kv_heads, head_dim, dtype == PKV_BF16,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int max_context_len,
+                                  int num_heads, int num_kv_heads, int head_dim, int dtype,
+                                  const pkv_decode_options *opts) {
+  if (shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                   dtype, opts) != PKV_OK)
+    return 0;
+  // sized for ragged q (q_lens given): the q_start table is then part of the workspace
+  return make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                   dtype, true, opts)
+      .bytes;
+}
+
+int pkv_decode_partition_size(int num_seqs, int total_q, int max_q_len, int max_context_len,
+                              int num_heads, int num_kv_heads, int head_dim, int dtype,
+                              const pkv_decode_options *opts) {
+  const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                              head_dim, dtype, opts);
+  if (st != PKV_OK) return st;
+  return make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                   dtype, true, opts)
+      .part_size;
+}
+
+int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          const int32_t *q_lens, void *out, float *lse, int num_seqs,
+                          int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
+                          int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
+                          int block_size, float scale, int dtype, const pkv_decode_options *opts,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                              head_dim, dtype, opts);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
+  if (!q_lens && (int64_t)num_seqs * max_q_len != total_q) return PKV_ERR_SHAPE;
+  if (q_lens && total_q < num_seqs) return PKV_ERR_SHAPE;
+
+  const bool bf16 = dtype == PKV_BF16;
+  const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                            head_dim, dtype, q_lens != nullptr, opts);
+  if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return PKV_ERR_WORKSPACE;
+  const int64_t units = (int64_t)num_kv_heads * pl.num_parts * num_seqs * pl.row_tiles;
+  if (units + 8 >= kMaxGrid || (int64_t)num_seqs * max_q_len * num_heads / 4 + 1 >= kMaxGrid)
+    return PKV_ERR_SHAPE;
+
+  char *ws = static_cast<char *>(workspace);
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.q_lens = q_lens;
+  a.q_start = pl.need_q_start ? reinterpret_cast<const int32_t *>(ws + pl.off_q_start) : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.part_lse = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
+  a.part_o = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.max_context_len = max_context_len;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.part_size = pl.part_size;
+  a.num_parts = pl.num_parts;
+  a.row_tiles = pl.row_tiles;
+  a.units = (int)units;
+  a.per_xcd = ceil_div(units, 8);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pl.need_q_start) {
+    if (pkv::launch_q_start(q_lens, reinterpret_cast<int32_t *>(ws + pl.off_q_start), num_seqs, s) !=
+        hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
+  if (opts && opts->event_main_begin &&
+      hipEventRecord(static_cast<hipEvent_t>(opts->event_main_begin), s) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  if (pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  if (opts && opts->event_main_end &&
+      hipEventRecord(static_cast<hipEvent_t>(opts->event_main_end), s) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  if (pl.num_parts > 1) {
+    if (pkv::launch_combine(a, bf16, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"
