@@ -167,10 +167,10 @@ def main():
     out = torch.empty_like(w.q)
     lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
     code = _lib.PKV_BF16 if spec.dtype == "bf16" else _lib.PKV_F32
-    P_used = _lib.decode_partition_size(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D,
-                                        code, P, path)
-    ws_bytes = _lib.decode_workspace_bytes(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D,
-                                           code, P, path)
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, P, path)
+    P_used = plan["partition_size"]
+    kernel = "decode_mfma_kernel" if plan["path"] == _lib.PATH_MFMA else "decode_valu_kernel"
+    ws_bytes = plan["workspace_bytes"]
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     q_lens = None if w.uniform_q else meta["q_lens"]
     stream = torch.cuda.current_stream()
@@ -208,7 +208,7 @@ def main():
     tokens = int(w.context_lens.astype(np.int64).sum())
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(spec.name, args.path)
+    traffic = measured_traffic(spec.name, kernel.split("_")[1])
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + attended tokens/s, 1 GPU",
         "value": round(value, 2),
@@ -226,7 +226,7 @@ def main():
             "workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
             "head_dim": D, "block_size": spec.block_size, "q_len": w.max_q_len,
             "context_tokens": tokens, "max_context_len": w.max_context_len, "partition_size": P_used,
-            "path": args.path, "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
+            "path": kernel.split("_")[1], "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
@@ -239,7 +239,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_valu_kernel" if args.path != "mfma" else "decode_mfma_kernel",
+            "kernel": kernel,
             "kernel_ms": round(k_ms, 5),
             "algorithmic_bytes_per_launch": dec_bytes,
         },

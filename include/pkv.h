@@ -98,11 +98,20 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int 
                                   int num_heads, int num_kv_heads, int head_dim, int dtype,
                                   const pkv_decode_options *opts);
 
-/* The partition size the library uses for these sizes and options (options->partition_size when it
- * is set, else the policy's choice).  Returns a negative pkv_status on bad sizes. */
-int pkv_decode_partition_size(int num_seqs, int total_q, int max_q_len, int max_context_len,
-                              int num_heads, int num_kv_heads, int head_dim, int dtype,
-                              const pkv_decode_options *opts);
+/* What the library will launch for these sizes and options. */
+typedef struct pkv_decode_plan_info {
+  int partition_size;      /* keys per partition */
+  int num_partitions;      /* ceil(max_context_len / partition_size) */
+  int path;                /* PKV_PATH_VALU or PKV_PATH_MFMA */
+  int rows_per_tile;       /* query rows (heads x new tokens of one kv head) per workgroup */
+  int row_tiles;           /* workgroups per (sequence, kv head, partition) */
+  size_t workspace_bytes;  /* same value as pkv_decode_workspace_bytes() */
+} pkv_decode_plan_info;
+
+/* Fills *info; returns PKV_OK or a negative pkv_status on bad sizes / options. */
+int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
+                    int num_kv_heads, int head_dim, int dtype, const pkv_decode_options *opts,
+                    pkv_decode_plan_info *info);
 
 /*
  * Paged decode attention (definition at the top of this file), with a split-K pass over key

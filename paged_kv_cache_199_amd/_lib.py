@@ -27,12 +27,17 @@ class DecodeOptions(ctypes.Structure):
                 ("event_main_begin", _vp), ("event_main_end", _vp)]
 
 
+class DecodePlanInfo(ctypes.Structure):
+    _fields_ = [("partition_size", _c_int), ("num_partitions", _c_int), ("path", _c_int),
+                ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("workspace_bytes", _c_sz)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = {
     "pkv_kv_cache_write": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp]),
     "pkv_decode_workspace_bytes": (_c_sz, [_c_int] * 8 + [ctypes.POINTER(DecodeOptions)]),
-    "pkv_decode_partition_size": (_c_int, [_c_int] * 8 + [ctypes.POINTER(DecodeOptions)]),
+    "pkv_decode_plan": (_c_int, [_c_int] * 8 + [ctypes.POINTER(DecodeOptions), ctypes.POINTER(DecodePlanInfo)]),
     "pkv_paged_attn_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                        _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
@@ -121,13 +126,15 @@ def decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_he
                                                  num_kv_heads, head_dim, dtype_code, ctypes.byref(o)))
 
 
-def decode_partition_size(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
-                          head_dim, dtype_code, partition_size=0, path=PATH_AUTO) -> int:
+def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                dtype_code, partition_size=0, path=PATH_AUTO) -> dict:
+    """What the library launches for these sizes: partition size, kernel path, row tiling, workspace."""
     o = DecodeOptions(partition_size, path, None, None)
-    rc = int(load().pkv_decode_partition_size(num_seqs, total_q, max_q_len, max_context_len, num_heads,
-                                              num_kv_heads, head_dim, dtype_code, ctypes.byref(o)))
-    _check(min(rc, 0), "pkv_decode_partition_size")
-    return rc
+    info = DecodePlanInfo()
+    rc = int(load().pkv_decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                                    head_dim, dtype_code, ctypes.byref(o), ctypes.byref(info)))
+    _check(rc, "pkv_decode_plan")
+    return {k: getattr(info, k) for k, _ in DecodePlanInfo._fields_}
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_combine.hip"]
+SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
+           "decode_combine.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

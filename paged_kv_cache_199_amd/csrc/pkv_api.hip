@@ -14,6 +14,8 @@ hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, v
 hipError_t launch_decode_valu(const DecodeArgs &a, bool bf16, int head_dim, int rows_per_tile,
                               hipStream_t st);
 int valu_max_rows(bool bf16);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, hipStream_t st);
+int mfma_rows_per_tile(int rows);
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 }  // namespace pkv
@@ -49,13 +51,16 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
   if (opts) {
     const int P = opts->partition_size;
     if (P < 0 || P % kBlockSize != 0) return PKV_ERR_UNSUPPORTED;
-    if (opts->path != PKV_PATH_AUTO && opts->path != PKV_PATH_VALU) return PKV_ERR_UNSUPPORTED;
+    if (opts->path != PKV_PATH_AUTO && opts->path != PKV_PATH_VALU && opts->path != PKV_PATH_MFMA)
+      return PKV_ERR_UNSUPPORTED;
+    if (opts->path == PKV_PATH_MFMA && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   }
   return PKV_OK;
 }
 
-// Policy.  Rows per tile: the whole GQA group times the new tokens when it fits the kernel's
-// register budget, else tiles.  Partition size: the largest of 512/256/128/64 keys that still gives
+// Policy.  Kernel: the matrix-core kernel for bf16, the vector-ALU kernel for fp32 (or when asked).
+// Rows per tile: the whole GQA group times the new tokens when it fits the kernel, else tiles.
+// Partition size: the largest of 512/256/128/64 keys that still gives
 // about 2048 live workgroups (8 per CU) for a mean context of half the maximum, and no split at all
 // when the whole context fits one partition.
 Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
@@ -65,10 +70,15 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   const bool bf16 = dtype == PKV_BF16;
   const int G = num_heads / num_kv_heads;
   const int rows = G * max_q_len;
-  pl.path = PKV_PATH_VALU;
-  const int rmax = pkv::valu_max_rows(bf16);
+  const int asked = opts ? opts->path : PKV_PATH_AUTO;
+  pl.path = asked == PKV_PATH_AUTO ? (bf16 ? PKV_PATH_MFMA : PKV_PATH_VALU) : asked;
   int R = 1;
-  while (R < rows && R < rmax) R <<= 1;
+  if (pl.path == PKV_PATH_MFMA) {
+    R = pkv::mfma_rows_per_tile(rows);
+  } else {
+    const int rmax = pkv::valu_max_rows(bf16);
+    while (R < rows && R < rmax) R <<= 1;
+  }
   pl.rows_per_tile = R;
   pl.row_tiles = ceil_div(rows, R);
   int P = opts ? opts->partition_size : 0;
@@ -147,15 +157,22 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int 
       .bytes;
 }
 
-int pkv_decode_partition_size(int num_seqs, int total_q, int max_q_len, int max_context_len,
-                              int num_heads, int num_kv_heads, int head_dim, int dtype,
-                              const pkv_decode_options *opts) {
+int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
+                    int num_kv_heads, int head_dim, int dtype, const pkv_decode_options *opts,
+                    pkv_decode_plan_info *info) {
+  if (!info) return PKV_ERR_NULL;
   const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                               head_dim, dtype, opts);
   if (st != PKV_OK) return st;
-  return make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
-                   dtype, true, opts)
-      .part_size;
+  const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                            head_dim, dtype, true, opts);
+  info->partition_size = pl.part_size;
+  info->num_partitions = pl.num_parts;
+  info->path = pl.path;
+  info->rows_per_tile = pl.rows_per_tile;
+  info->row_tiles = pl.row_tiles;
+  info->workspace_bytes = pl.bytes;
+  return PKV_OK;
 }
 
 int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -221,7 +238,10 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   if (opts && opts->event_main_begin &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_begin), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
-  if (pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  const hipError_t le = pl.path == PKV_PATH_MFMA
+                           ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, s)
+                           : pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s);
+  if (le != hipSuccess) return PKV_ERR_LAUNCH;
   if (opts && opts->event_main_end &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_end), s) != hipSuccess)
     return PKV_ERR_LAUNCH;

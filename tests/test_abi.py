@@ -65,6 +65,8 @@ def test_decode_argument_validation(lib):
     assert _decode(lib, **full, opts=ctypes.byref(bad_p)) == -3  # partition not a multiple of 16
     bad_path = _lib.DecodeOptions(0, 9, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(bad_path)) == -3
+    mfma_f32 = _lib.DecodeOptions(0, _lib.PATH_MFMA, None, None)
+    assert _decode(lib, **full, opts=ctypes.byref(mfma_f32)) == -3   # matrix-core path is bf16 only
     # a split launch needs workspace
     small_p = _lib.DecodeOptions(16, 0, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(small_p)) == -4
@@ -74,15 +76,21 @@ def test_decode_argument_validation(lib):
 def test_workspace_and_partition_policy(lib):
     o = _lib.DecodeOptions(0, 0, None, None)
     # long contexts split into 512-key partitions with fp32 partials
-    P = lib.pkv_decode_partition_size(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o))
-    assert P == 512
+    info = _lib.DecodePlanInfo()
+    assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o), ctypes.byref(info)) == 0
+    assert info.partition_size == 512 and info.num_partitions == 64
+    assert info.path == _lib.PATH_MFMA and info.rows_per_tile == 16 and info.row_tiles == 1
     ws = lib.pkv_decode_workspace_bytes(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o))
     assert ws >= 64 * 256 * 64 * (128 + 1) * 4
     # a context that fits one partition needs no partials
     o1 = _lib.DecodeOptions(4096, 0, None, None)
-    assert lib.pkv_decode_partition_size(4, 4, 1, 40, 4, 2, 64, 0, ctypes.byref(o1)) == 48
+    assert lib.pkv_decode_plan(4, 4, 1, 40, 4, 2, 64, 0, ctypes.byref(o1), ctypes.byref(info)) == 0
+    assert info.partition_size == 48 and info.num_partitions == 1 and info.path == _lib.PATH_VALU
     assert lib.pkv_decode_workspace_bytes(4, 4, 1, 40, 4, 2, 64, 0, ctypes.byref(o1)) < 4096
-    assert lib.pkv_decode_partition_size(4, 4, 1, 40, 4, 3, 64, 0, None) == -2
+    assert lib.pkv_decode_plan(4, 4, 1, 40, 4, 3, 64, 0, None, ctypes.byref(info)) == -2
+    # speculative verify: 4 heads x 5 new tokens = 20 rows -> two 16-row tiles in one workgroup
+    assert lib.pkv_decode_plan(32, 160, 5, 8192, 32, 8, 128, 1, None, ctypes.byref(info)) == 0
+    assert info.rows_per_tile == 32 and info.row_tiles == 1
 
 
 def test_write_argument_validation(lib):

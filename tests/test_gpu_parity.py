@@ -21,6 +21,16 @@ def _say(*a):
     print(*a, flush=True)
 
 
+def _paths(w):
+    """Every kernel family that serves this dtype."""
+    return (_lib.PATH_VALU, _lib.PATH_MFMA) if w.spec.dtype == "bf16" else (_lib.PATH_VALU,)
+
+
+def _check_all(w, partition_size=0, strict=None):
+    for path in _paths(w):
+        _check_full(w, partition_size, path, strict)
+
+
 def _check_full(w, partition_size=0, path=_lib.PATH_AUTO, strict=None):
     _say(f"[case] {w.spec.name} P={partition_size} path={path}")
     out, lse = run_library(w, DEV, partition_size=partition_size, path=path)
@@ -51,24 +61,22 @@ def test_conc32_write_then_decode(gpu_lib):
     want_k, want_v = O.kv_cache_write(kc0, vc0, host_bits(w.new_k), host_bits(w.new_v), w.slot_mapping)
     assert np.array_equal(host_bits(w.k_cache), want_k)
     assert np.array_equal(host_bits(w.v_cache), want_v)
-    _check_full(w)
+    _check_all(w)
 
 
 @pytest.mark.parametrize("P", [0, 512])
 def test_shared_prefix(gpu_lib, P):
-    _check_full(W.build(2, DEV), P)
+    _check_all(W.build(2, DEV), P)
 
 
 def test_spec_verify(gpu_lib):
-    _check_full(W.build(3, DEV))
+    _check_all(W.build(3, DEV))
 
 
 def test_long_context_splitk_sampled(gpu_lib):
     """Full-size long-context workload in the benchmark's launch configuration (512-key partitions),
     checked on sampled sequences: the longest, the shortest and a seeded spread."""
     w = W.build(4, DEV)
-    _say("[case] long_ctx_splitk_bf16 P=512 (full size)")
-    out, lse = run_library(w, DEV, partition_size=512)
     order = np.argsort(w.context_lens)
     rng = np.random.default_rng(5)
     seqs = sorted(set([int(order[0]), int(order[-1]), int(order[-2])] +
@@ -76,13 +84,15 @@ def test_long_context_splitk_sampled(gpu_lib):
     ref_out, ref_lse = oracle_sampled(w, seqs)
     rows = np.zeros(w.total_q, dtype=bool)
     rows[seqs] = True
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, rows=rows)
     _say(f"   seqs {seqs} ctx {[int(w.context_lens[s]) for s in seqs]}")
-    _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
-    assert d_out <= BF16_TOL and d_lse <= LSE_TOL
-    # a property that holds for every row, sampled or not: finite output and LSE
-    got = out.float()
-    assert torch.isfinite(got).all() and torch.isfinite(lse).all()
+    for path in _paths(w):
+        _say(f"[case] long_ctx_splitk_bf16 P=512 (full size) path={path}")
+        out, lse = run_library(w, DEV, partition_size=512, path=path)
+        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, rows=rows)
+        _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+        assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+        # a property that holds for every row, sampled or not: finite output and LSE
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
 EDGE_CTX = [1, 15, 16, 17, 511, 512, 513, 1024, 1025]
@@ -94,7 +104,7 @@ def test_edge_context_lengths(gpu_lib, dtype, D):
     spec = W.custom(f"edge_ctx_{dtype}_{D}", EDGE_CTX, num_heads=8, num_kv_heads=2, head_dim=D, dtype=dtype)
     w = W.build(spec, DEV)
     for P in (0, 16, 512, 2048):
-        _check_full(w, P)
+        _check_all(w, P)
 
 
 @pytest.mark.parametrize("q", [2, 3, 4, 5])
@@ -103,7 +113,7 @@ def test_edge_multi_query(gpu_lib, q):
     spec = W.custom(f"edge_q{q}", ctx, q_len=q, num_heads=8, num_kv_heads=2, head_dim=128)
     w = W.build(spec, DEV)
     for P in (0, 16, 512):
-        _check_full(w, P)
+        _check_all(w, P)
 
 
 def test_ragged_q_lens(gpu_lib):
@@ -112,13 +122,13 @@ def test_ragged_q_lens(gpu_lib):
     spec = W.custom("ragged_q", ctx, q_len=ql, num_heads=16, num_kv_heads=4, head_dim=64)
     w = W.build(spec, DEV)
     for P in (0, 32, 512):
-        _check_full(w, P)
+        _check_all(w, P)
 
 
 def test_gqa8_and_mha(gpu_lib):
     for H, KVH in ((64, 8), (8, 8), (16, 1)):
         spec = W.custom(f"heads_{H}_{KVH}", [100, 700, 1500], num_heads=H, num_kv_heads=KVH, head_dim=128)
-        _check_full(W.build(spec, DEV))
+        _check_all(W.build(spec, DEV))
 
 
 def test_poisoned_unread_slots_do_not_leak(gpu_lib):
@@ -128,25 +138,27 @@ def test_poisoned_unread_slots_do_not_leak(gpu_lib):
                         num_kv_heads=2, head_dim=64, dtype=dtype)
         w = W.build(spec, DEV, poison=True)
         for P in (0, 16, 512):
-            _check_full(w, P)
+            _check_all(w, P)
 
 
-def test_repeat_is_bitwise_deterministic(gpu_lib):
+@pytest.mark.parametrize("path", [_lib.PATH_VALU, _lib.PATH_MFMA])
+def test_repeat_is_bitwise_deterministic(gpu_lib, path):
     w = W.build(3, DEV)
-    a, la = run_library(w, DEV)
-    b, lb = run_library(w, DEV)
+    a, la = run_library(w, DEV, path=path)
+    b, lb = run_library(w, DEV, path=path)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
-def test_physical_block_permutation_is_bitwise_invisible(gpu_lib):
+@pytest.mark.parametrize("path", [_lib.PATH_VALU, _lib.PATH_MFMA])
+def test_physical_block_permutation_is_bitwise_invisible(gpu_lib, path):
     w = W.build(1, DEV)
-    a, la = run_library(w, DEV)
+    a, la = run_library(w, DEV, path=path)
     perm = np.random.default_rng(3).permutation(w.num_blocks)
     inv = torch.from_numpy(np.argsort(perm)).to(DEV)
     kc2 = w.k_cache.index_select(0, inv)          # kc2[perm[b]] = kc[b]
     vc2 = w.v_cache.index_select(0, inv)
     w.block_tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
-    b, lb = run_library(w, DEV, k_cache=kc2, v_cache=vc2)
+    b, lb = run_library(w, DEV, k_cache=kc2, v_cache=vc2, path=path)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
