@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--workload", default="conc32_bf16")
     ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own, 0: policy")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--depth", type=int, default=0, help="MFMA register ring depth (0: policy)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -167,9 +169,13 @@ def main():
     out = torch.empty_like(w.q)
     lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
     code = _lib.PKV_BF16 if spec.dtype == "bf16" else _lib.PKV_F32
-    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, P, path)
+    sched = {"auto": 0, "grid": 1, "persistent": 2}[args.schedule]
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, P, path,
+                            args.depth, sched)
     P_used = plan["partition_size"]
-    kernel = "decode_mfma_kernel" if plan["path"] == _lib.PATH_MFMA else "decode_valu_kernel"
+    kernel = "decode_valu_kernel"
+    if plan["path"] == _lib.PATH_MFMA:
+        kernel = "decode_mfma_persistent_kernel" if plan["schedule"] == 2 else "decode_mfma_kernel"
     ws_bytes = plan["workspace_bytes"]
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     q_lens = None if w.uniform_q else meta["q_lens"]
@@ -186,7 +192,8 @@ def main():
             _lib.kv_cache_write(w.new_k, w.new_v, meta["slot_mapping"], kcs[r], vcs[r])
         _lib.paged_attn_decode(w.q, kcs[r], vcs[r], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
                                H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
-                               partition_size=P, path=path, workspace=ws, events=events)
+                               partition_size=P, path=path, workspace=ws, events=events, depth=args.depth,
+                               schedule=sched)
 
     for i in range(args.warmup):
         step(i)
@@ -226,7 +233,8 @@ def main():
             "workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
             "head_dim": D, "block_size": spec.block_size, "q_len": w.max_q_len,
             "context_tokens": tokens, "max_context_len": w.max_context_len, "partition_size": P_used,
-            "path": kernel.split("_")[1], "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
+            "path": kernel.split("_")[1], "schedule": ["", "grid", "persistent"][plan["schedule"]],
+            "pipeline_depth": plan["pipeline_depth"], "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

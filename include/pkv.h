@@ -64,11 +64,22 @@ typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 /* Kernel family for the partition pass.  AUTO lets the library choose. */
 typedef enum pkv_path { PKV_PATH_AUTO = 0, PKV_PATH_VALU = 1, PKV_PATH_MFMA = 2 } pkv_path;
 
+/* How partition work maps onto the GPU (matrix-core kernel).  GRID: one workgroup per (kv head,
+ * partition, sequence, row tile) of a grid sized from the host maxima.  PERSISTENT: a few workgroups
+ * per CU whose waves walk the live partitions listed from context_lens (num_seqs <= 4096, partitions
+ * of at most 1024 keys).  AUTO lets the library choose. */
+typedef enum pkv_schedule {
+  PKV_SCHEDULE_AUTO = 0, PKV_SCHEDULE_GRID = 1, PKV_SCHEDULE_PERSISTENT = 2
+} pkv_schedule;
+
 /* Optional tuning / instrumentation for pkv_paged_attn_decode.  Pass NULL for defaults; a zeroed
  * struct also means defaults. */
 typedef struct pkv_decode_options {
-  int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy */
+  int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy;
+                               values above 4096 (1024 for the persistent schedule) are clamped */
   int path;                 /* pkv_path */
+  int pipeline_depth;       /* MFMA kernel: pages of K/V held per wave (2..4); 0 = policy */
+  int schedule;             /* pkv_schedule */
   void *event_main_begin;   /* hipEvent_t recorded on `stream` right before the partition kernel */
   void *event_main_end;     /* hipEvent_t recorded right after it (before the combine kernel) */
 } pkv_decode_options;
@@ -105,6 +116,8 @@ typedef struct pkv_decode_plan_info {
   int path;                /* PKV_PATH_VALU or PKV_PATH_MFMA */
   int rows_per_tile;       /* query rows (heads x new tokens of one kv head) per workgroup */
   int row_tiles;           /* workgroups per (sequence, kv head, partition) */
+  int pipeline_depth;      /* MFMA kernel register ring depth */
+  int schedule;            /* PKV_SCHEDULE_GRID or PKV_SCHEDULE_PERSISTENT */
   size_t workspace_bytes;  /* same value as pkv_decode_workspace_bytes() */
 } pkv_decode_plan_info;
 

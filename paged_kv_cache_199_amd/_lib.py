@@ -17,19 +17,21 @@ LIB_PATH = os.path.join(_PKG, "libpkv.so")
 
 PKV_F32, PKV_BF16 = 0, 1
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_GRID, SCHEDULE_PERSISTENT = 0, 1, 2
 BLOCK_SIZE = 16
 
 _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
 
 class DecodeOptions(ctypes.Structure):
-    _fields_ = [("partition_size", _c_int), ("path", _c_int),
-                ("event_main_begin", _vp), ("event_main_end", _vp)]
+    _fields_ = [("partition_size", _c_int), ("path", _c_int), ("pipeline_depth", _c_int),
+                ("schedule", _c_int), ("event_main_begin", _vp), ("event_main_end", _vp)]
 
 
 class DecodePlanInfo(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("num_partitions", _c_int), ("path", _c_int),
-                ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("workspace_bytes", _c_sz)]
+                ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("pipeline_depth", _c_int),
+                ("schedule", _c_int), ("workspace_bytes", _c_sz)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -91,8 +93,8 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _opts(partition_size: int, path: int, events) -> DecodeOptions:
-    o = DecodeOptions(partition_size, path, None, None)
+def _opts(partition_size: int, path: int, events, depth: int = 0, schedule: int = 0) -> DecodeOptions:
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
     if events is not None:
         b, e = events
         o.event_main_begin = b.cuda_event
@@ -120,16 +122,17 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 
 def decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
-                           head_dim, dtype_code, partition_size=0, path=PATH_AUTO) -> int:
-    o = DecodeOptions(partition_size, path, None, None)
+                           head_dim, dtype_code, partition_size=0, path=PATH_AUTO, depth=0,
+                           schedule=0) -> int:
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
     return int(load().pkv_decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads,
                                                  num_kv_heads, head_dim, dtype_code, ctypes.byref(o)))
 
 
 def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
-                dtype_code, partition_size=0, path=PATH_AUTO) -> dict:
+                dtype_code, partition_size=0, path=PATH_AUTO, depth=0, schedule=0) -> dict:
     """What the library launches for these sizes: partition size, kernel path, row tiling, workspace."""
-    o = DecodeOptions(partition_size, path, None, None)
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
     info = DecodePlanInfo()
     rc = int(load().pkv_decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                                     head_dim, dtype_code, ctypes.byref(o), ctypes.byref(info)))
@@ -143,7 +146,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       num_heads: int, num_kv_heads: int, head_dim: int, block_size: int, scale: float,
                       max_context_len: int, max_q_len: int = 1, partition_size: int = 0,
                       path: int = PATH_AUTO, workspace: Optional[torch.Tensor] = None,
-                      events=None, stream=None) -> None:
+                      events=None, stream=None, depth: int = 0, schedule: int = 0) -> None:
     """Decode attention through the C ABI.  q/out [total_q, H, D]; lse fp32 [total_q, H] or None.
 
     q_lens None means every sequence has max_q_len new tokens.  max_context_len is a host-known upper
@@ -170,7 +173,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
               "lse: fp32 [total_q, H]")
     code = _dtype_code(q)
-    o = _opts(partition_size, path, events)
+    o = _opts(partition_size, path, events, depth, schedule)
     need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                               num_kv_heads, head_dim, code, ctypes.byref(o)))
     if workspace is None and need > 0:

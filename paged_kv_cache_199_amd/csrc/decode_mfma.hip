@@ -1,41 +1,29 @@
-// Paged decode attention, matrix-core (MFMA) partition kernel for bf16 K/V.
+// Paged decode attention on the matrix cores (bf16 K/V): the partition pass.
 //
-// Same operation and work units as the vector-ALU kernel (GQA decode over K/V gathered through the
-// block table, one key partition per workgroup, online softmax; inferd page: paged-attention
-// reference beside the page table; lfm25-inference page, "Runtime Design": paged GQA/XQA decode with
-// split-K).  The rows that share a kv head (G query heads times the new tokens) form the N side of
-// two small matrix products per 16-token page:
+// Operation: GQA decode attention over K/V gathered through the block table, one key partition at a
+// time, online softmax (inferd page: paged-attention reference beside the page table; lfm25-inference
+// page, "Runtime Design": paged GQA/XQA decode with split-K).  A sequence that fits one partition gets
+// its final output and LSE here; otherwise each partition leaves a normalized fp32 partial and its
+// log2-sum-exp for the combine kernel.  The per-wave matrix-core work lives in mfma_wave.h.
 //
-//   S^T[t][r] = sum_d K[t][d] Q[r][d]      v_mfma_f32_16x16x32_bf16, D/32 steps
-//   O^T[d][r] += sum_t V^T[d][t] P^T[t][r]  v_mfma_f32_16x16x16_bf16, one per 16 output dims
-//
-// The 16x16 accumulator layout (lane l holds column l % 16, rows 4*(l/16) .. +3) makes the score
-// tile of one product the B operand of the next: after the softmax each lane packs its own four
-// probabilities to bf16 and feeds them straight into the P.V product, with no lane exchange.  The
-// V^T operand wants four consecutive tokens of one dim per lane, which is why V pages are stored
-// dim-major.  Rows are 16 per N tile; up to two N tiles (32 rows) share each page's K/V registers.
-//
-// Pipelining: each wave preloads the physical ids of all pages it will visit (one per lane) and
-// issues the next page's K and V loads before computing on the current page.
-#include "decode_args.h"
-#include "device_common.h"
+// Two schedules:
+//  * grid: one 4-wave workgroup per (kv head, partition, sequence, row tile) of a dense grid sized from
+//    the host-known maxima; workgroups past a sequence's end exit at once.  The waves of a workgroup
+//    take every fourth page of the partition and merge through LDS.
+//  * persistent: a grid of a few workgroups per CU.  Every workgroup lists the live work items from
+//    context_lens into LDS (items are (kv head, sequence, partition, row tile), kv-head-major), the
+//    8 XCDs take equal contiguous shares of the list, and every wave is an independent worker that
+//    takes every W-th item of its XCD's share and attends the whole partition itself.  No workgroup
+//    is spent on an empty partition, ragged lengths spread evenly over all waves, and the items that
+//    read one kv head's pages (including prefix pages several sequences share) stay under one L2.
+#include "mfma_wave.h"
 
 namespace pkv {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-
-template <int D, int NT>
+template <int D, int NT, int NBUF>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NW = 4;
-  constexpr int ROWB = D * 2;          // bytes of a K token row / a V dim row pair... (bf16)
-  constexpr int NK = D / 32;           // QK k-steps
-  constexpr int ND = D / 16;           // PV output tiles
+  constexpr int ND = D / 16;
   constexpr int ROWS = 16 * NT;
 
   __shared__ float mrg_acc[NW][ROWS][D];
@@ -44,8 +32,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;           // N index (row of the tile) this lane owns
-  const int grp = lane >> 4;           // k-group / 4-row group
+  const int col = lane & 15;
+  const int grp = lane >> 4;
 
   int u = xcd_unit(blockIdx.x, a.per_xcd);
   if (u >= a.units) return;
@@ -62,168 +50,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int rows = si.qs * G;
   const int row0 = rt * ROWS;
   if (row0 >= rows) return;
-  const int H = a.num_heads;
-  const int KVH = a.num_kv_heads;
 
-  // ---- the rows this lane's column stands for, one per N tile
-  int last[NT];
-  bf16x8_t qB[NT][NK];
-  #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int rr = row0 + n * 16 + col;
-    const int i = rr / G;
-    const int qrow = si.qbase + i;
-    const int head = kvh * G + (rr - i * G);
-    const bool ok = rr < rows && qrow < a.total_q;
-    last[n] = ok ? si.ctx - si.qs + i : -1;
-    const char *qp = static_cast<const char *>(a.q) + ((int64_t)qrow * H + head) * ROWB;
-    #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      const uint4 w = ok ? ld16(qp + (4 * c + grp) * 16) : make_uint4(0, 0, 0, 0);
-      qB[n][c] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-  const int first_last = si.ctx - si.qs + row0 / G;   // fewest visible keys among the tile's rows
-
-  float m[NT], lsum[NT];
-  float4_t acc[NT][ND];
-  #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    m[n] = kNegBig;
-    lsum[n] = 0.f;
-    #pragma unroll
-    for (int t = 0; t < ND; ++t) acc[n][t] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  WaveRows<D, NT> w;
+  load_rows<D, NT>(a, si, kvh, row0, rows, col, grp, w);
+  WaveAcc<D, NT> st;
+  init_acc<D, NT>(st);
 
   const int tok0 = p * a.part_size;
   const int tok1 = min(si.ctx, tok0 + a.part_size);
   const int blk0 = tok0 / kBlock;
   const int nblk = (tok1 - tok0 + kBlock - 1) / kBlock;
   const int niter = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
-  const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq + blk0 + wave;
-  const char *kbase = static_cast<const char *>(a.k_cache);
-  const char *vbase = static_cast<const char *>(a.v_cache);
-  const int64_t page_bytes = (int64_t)kBlock * ROWB;
-  const int64_t nb = a.num_blocks;
-
-  // page ids of iterations [base, base + 64), one per lane
-  int ids = 0;
-  auto load_ids = [&](int base) {
-    const int k = base + lane;
-    ids = k < niter ? bt[(int64_t)NW * k] : 0;
-  };
-  auto page_of = [&](int it, bool &ok) -> int64_t {
-    int bid = __builtin_amdgcn_readlane(ids, it & 63);
-    ok = bid >= 0 && bid < nb;
-    return ((int64_t)(ok ? bid : 0) * KVH + kvh) * page_bytes;
-  };
-  uint4 kC[NK], kN[NK];
-  uint2 vC[ND], vN[ND];
-  bool okC = true, okN = true;
-  auto issue = [&](int it, uint4 *kr, uint2 *vr, bool &ok) {
-    const int64_t off = page_of(it, ok);
-    const char *kp = kbase + off + col * ROWB + grp * 16;
-    #pragma unroll
-    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
-    const char *vp = vbase + off + (col * kBlock + 4 * grp) * 2;
-    #pragma unroll
-    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
-  };
-
-  if (niter > 0) {
-    load_ids(0);
-    issue(0, kC, vC, okC);
-  }
-  for (int it = 0; it < niter; ++it) {
-    if (it + 1 < niter) {
-      if (((it + 1) & 63) == 0) load_ids(it + 1);
-      issue(it + 1, kN, vN, okN);
-    }
-    // S^T for this page: lane holds tokens 4*grp .. +3 of its column's row
-    float4_t sc[NT];
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float4_t c4 = {0.f, 0.f, 0.f, 0.f};
-      #pragma unroll
-      for (int c = 0; c < NK; ++c)
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kC[c]), qB[n][c], c4, 0, 0, 0);
-      sc[n] = c4 * a.scale_log2;
-    }
-    const int bstart = (blk0 + wave + it * NW) * kBlock;
-    if (!okC || bstart + kBlock > first_last + 1) {
-      const int pos0 = bstart + 4 * grp;
-      #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!okC || pos0 + e > last[n]) sc[n][e] = -INFINITY;
-      }
-      const int valid = okC ? si.ctx - bstart : 0;
-      if (valid < kBlock) {
-        // slots past the context may hold anything: zero them so p = 0 contributes exactly 0
-        #pragma unroll
-        for (int t = 0; t < ND; ++t) {
-          if (4 * grp >= valid) vC[t].x = 0u;
-          else if (4 * grp + 1 >= valid) vC[t].x &= 0xffffu;
-          if (4 * grp + 2 >= valid) vC[t].y = 0u;
-          else if (4 * grp + 3 >= valid) vC[t].y &= 0xffffu;
-        }
-      }
-    }
-    bool need = false;
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float th = m[n] + kRescaleSlack;
-      need |= sc[n][0] > th || sc[n][1] > th || sc[n][2] > th || sc[n][3] > th;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float bm = fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m[n], bm);
-        const float alpha = exp2_hw(m[n] - mn);
-        m[n] = mn;
-        lsum[n] *= alpha;
-        #pragma unroll
-        for (int t = 0; t < ND; ++t) acc[n][t] *= alpha;
-      }
-    }
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float p0 = exp2_hw(sc[n][0] - m[n]);
-      const float p1 = exp2_hw(sc[n][1] - m[n]);
-      const float p2 = exp2_hw(sc[n][2] - m[n]);
-      const float p3 = exp2_hw(sc[n][3] - m[n]);
-      lsum[n] += (p0 + p1) + (p2 + p3);
-      const uint2 pw = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
-      const short4_t pB = __builtin_bit_cast(short4_t, pw);
-      #pragma unroll
-      for (int t = 0; t < ND; ++t)
-        acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vC[t]), pB,
-                                                              acc[n][t], 0, 0, 0);
-    }
-    #pragma unroll
-    for (int c = 0; c < NK; ++c) kC[c] = kN[c];
-    #pragma unroll
-    for (int t = 0; t < ND; ++t) vC[t] = vN[t];
-    okC = okN;
-  }
+  const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  attend_pages<D, NT, NBUF>(a, si, kvh, bt, blk0 + wave, NW, niter, lane, w, st);
 
   // ---- per-wave state to LDS, then merge the waves
   #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    float l = lsum[n];
+    float l = st.lsum[n];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     #pragma unroll
     for (int t = 0; t < ND; ++t) {
       #pragma unroll
-      for (int e = 0; e < 4; ++e) mrg_acc[wave][n * 16 + col][t * 16 + 4 * grp + e] = acc[n][t][e];
+      for (int e = 0; e < 4; ++e) mrg_acc[wave][n * 16 + col][t * 16 + 4 * grp + e] = st.acc[n][t][e];
     }
     if (grp == 0) {
-      mrg_m[wave][n * 16 + col] = m[n];
+      mrg_m[wave][n * 16 + col] = st.m[n];
       mrg_l[wave][n * 16 + col] = l;
     }
   }
@@ -241,42 +94,200 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int head = kvh * G + (rr - i * G);
     float M = mrg_m[0][r];
     #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, mrg_m[w][r]);
+    for (int q = 1; q < NW; ++q) M = fmaxf(M, mrg_m[q][r]);
     float L = 0.f, O = 0.f;
     #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sw = exp2_hw(mrg_m[w][r] - M);
-      L += mrg_l[w][r] * sw;
-      O += mrg_acc[w][r][d] * sw;
+    for (int q = 0; q < NW; ++q) {
+      const float sw = exp2_hw(mrg_m[q][r] - M);
+      L += mrg_l[q][r] * sw;
+      O += mrg_acc[q][r][d] * sw;
     }
     const bool seen = L > 0.f;
     const float o = seen ? O / L : 0.f;
     const float lse2 = seen ? M + log2_hw(L) : -INFINITY;
-    const int64_t orow = (int64_t)qrow * H + head;
+    const int64_t orow = (int64_t)qrow * a.num_heads + head;
     if (single) {
       static_cast<uint16_t *>(a.out)[orow * D + d] = f32_to_bf16(o);
       if (d == 0 && a.lse) a.lse[orow] = lse2 * kLn2;
     } else {
-      const int64_t prow = (int64_t)p * a.total_q * H + orow;
+      const int64_t prow = (int64_t)p * a.total_q * a.num_heads + orow;
       a.part_o[prow * D + d] = o;
       if (d == 0) a.part_lse[prow] = lse2;
     }
   }
 }
 
-// Rows one launch covers per workgroup: 16 per N tile, at most two N tiles.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+  #pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// LDS tables of the persistent schedule, per sequence s: pre = items of sequences < s (for one kv
+// head), ctx = clamped context length, qb = first q row, rts = row tiles, qs = clamped new tokens.
+template <int D, int NT, int NBUF>
+__global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs a) {
+  constexpr int ROWS = 16 * NT;
+  extern __shared__ int sh[];
+  const int S = a.num_seqs;
+  int *pre = sh;              // [S + 1]
+  int *tctx = sh + S + 1;     // [S]
+  int *tqb = tctx + S;        // [S]
+  int *trts = tqb + S;        // [S]
+  int *tqs = trts + S;        // [S]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int G = a.group;
+
+  if (wave == 0) {
+    int run_items = 0, run_q = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int s = base + lane;
+      int ctx = 0, qs = 0, qraw = 0, items = 0, rt = 1;
+      if (s < S) {
+        ctx = min(min(a.context_lens[s], a.max_context_len), a.max_blocks_per_seq * kBlock);
+        ctx = max(ctx, 0);
+        qraw = max(a.q_lens ? a.q_lens[s] : a.max_q_len, 0);
+        qs = max(1, min(qraw, ctx));
+        rt = (qs * G + ROWS - 1) / ROWS;
+        items = (ctx + a.part_size - 1) / a.part_size * rt;
+      }
+      const int inc_items = wave_incl_scan(items, lane);
+      const int inc_q = wave_incl_scan(qraw, lane);
+      if (s < S) {
+        pre[s + 1] = run_items + inc_items;
+        tctx[s] = ctx;
+        tqb[s] = run_q + inc_q - qraw;
+        trts[s] = rt;
+        tqs[s] = qs;
+      }
+      run_items += __shfl(inc_items, 63);
+      run_q += __shfl(inc_q, 63);
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+
+  const int I = pre[S];                             // items per kv head
+  const int64_t L = (int64_t)I * a.num_kv_heads;    // all items
+  const int xcd = blockIdx.x & 7;
+  const int n_wg = (int)((gridDim.x - xcd + 7) >> 3);
+  const int64_t lo = L * xcd / 8;
+  const int64_t hi = L * (xcd + 1) / 8;
+  const int W = n_wg * 4;
+  for (int64_t k = lo + (blockIdx.x >> 3) * 4 + wave; k < hi; k += W) {
+    const int kvh = (int)(k / I);
+    const int r = (int)(k - (int64_t)kvh * I);
+    int s0 = 0, s1 = S;                              // pre[s0] <= r < pre[s1]
+    while (s1 - s0 > 1) {
+      const int mid = (s0 + s1) >> 1;
+      if (pre[mid] <= r) s0 = mid;
+      else s1 = mid;
+    }
+    const int s = s0;
+    const int local = r - pre[s];
+    const int rts = trts[s];
+    const int p = local / rts;
+    const int rt = local - p * rts;
+    SeqInfo si;
+    si.ctx = tctx[s];
+    si.qs = tqs[s];
+    si.qbase = tqb[s];
+    si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
+
+    WaveRows<D, NT> w;
+    load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
+    WaveAcc<D, NT> st;
+    init_acc<D, NT>(st);
+    const int tok0 = p * a.part_size;
+    const int tok1 = min(si.ctx, tok0 + a.part_size);
+    const int npages = (tok1 - tok0 + kBlock - 1) / kBlock;
+    attend_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq,
+                              tok0 / kBlock, 1, npages, lane, w, st);
+    finish_wave<D, NT>(a, p, si.nparts == 1, lane, w, st);
+  }
+}
+
+// Rows one launch covers per work item: 16 per N tile, at most two N tiles.
 int mfma_rows_per_tile(int rows) { return rows > 16 ? 32 : 16; }
 
-hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, hipStream_t st) {
-  const int grid = a.per_xcd * 8;
-  if (head_dim == 64) {
-    if (rows_per_tile > 16) decode_mfma_kernel<64, 2><<<grid, 256, 0, st>>>(a);
-    else decode_mfma_kernel<64, 1><<<grid, 256, 0, st>>>(a);
+// Pages in flight per wave = depth - 1.  Depths 2..4 are built.
+int mfma_default_depth(int head_dim, int rows_per_tile) { return 3; }
+
+// Largest batch the persistent schedule lists in LDS, and the LDS it needs.
+int persistent_max_seqs() { return 4096; }
+size_t persistent_lds_bytes(int num_seqs) { return (size_t)(5 * num_seqs + 1) * sizeof(int); }
+
+template <int D, int NT, int NBUF>
+static hipError_t launch_one(const DecodeArgs &a, bool persistent, int grid, hipStream_t st) {
+  if (persistent) {
+    decode_mfma_persistent_kernel<D, NT, NBUF><<<grid, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
   } else {
-    if (rows_per_tile > 16) decode_mfma_kernel<128, 2><<<grid, 256, 0, st>>>(a);
-    else decode_mfma_kernel<128, 1><<<grid, 256, 0, st>>>(a);
+    decode_mfma_kernel<D, NT, NBUF><<<a.per_xcd * 8, 256, 0, st>>>(a);
   }
   return hipGetLastError();
+}
+
+template <int D, int NT>
+static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent, int grid,
+                                 hipStream_t st) {
+  switch (depth) {
+    case 2: return launch_one<D, NT, 2>(a, persistent, grid, st);
+    case 4: return launch_one<D, NT, 4>(a, persistent, grid, st);
+    default: return launch_one<D, NT, 3>(a, persistent, grid, st);
+  }
+}
+
+// Workgroups of one persistent-kernel instance that fit a CU at once.
+template <int D, int NT, int NBUF>
+static int occupancy_of(int num_seqs) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_persistent_kernel<D, NT, NBUF>, 256,
+                                                   persistent_lds_bytes(num_seqs)) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int D, int NT>
+static int occupancy_dn(int depth, int num_seqs) {
+  switch (depth) {
+    case 2: return occupancy_of<D, NT, 2>(num_seqs);
+    case 4: return occupancy_of<D, NT, 4>(num_seqs);
+    default: return occupancy_of<D, NT, 3>(num_seqs);
+  }
+}
+
+// Cached per (head_dim, N tiles, depth) and per LDS size class (the tables grow with the batch).
+int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs) {
+  static int cache[2][2][5][4];
+  const int di = head_dim == 64 ? 0 : 1;
+  const int ni = rows_per_tile > 16 ? 1 : 0;
+  const int ci = num_seqs <= 512 ? 0 : num_seqs <= 1024 ? 1 : num_seqs <= 2048 ? 2 : 3;
+  const int sz = ci == 0 ? 512 : ci == 1 ? 1024 : ci == 2 ? 2048 : 4096;
+  int &slot = cache[di][ni][depth][ci];
+  if (slot <= 0) {
+    if (head_dim == 64)
+      slot = rows_per_tile > 16 ? occupancy_dn<64, 2>(depth, sz) : occupancy_dn<64, 1>(depth, sz);
+    else
+      slot = rows_per_tile > 16 ? occupancy_dn<128, 2>(depth, sz) : occupancy_dn<128, 1>(depth, sz);
+  }
+  return slot;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, int depth,
+                              bool persistent, int grid, hipStream_t st) {
+  if (head_dim == 64) {
+    return rows_per_tile > 16 ? launch_mfma_dn<64, 2>(a, depth, persistent, grid, st)
+                              : launch_mfma_dn<64, 1>(a, depth, persistent, grid, st);
+  }
+  return rows_per_tile > 16 ? launch_mfma_dn<128, 2>(a, depth, persistent, grid, st)
+                            : launch_mfma_dn<128, 1>(a, depth, persistent, grid, st);
 }
 
 }  // namespace pkv

@@ -1,0 +1,240 @@
+// One wave's share of paged decode attention on the matrix cores (bf16 K/V), shared by the
+// one-workgroup-per-partition kernel and the persistent kernel.
+//
+// A wave owns up to 16 * NT query rows that read one kv head (the G query heads sharing it times the
+// sequence's new tokens; row r -> token r / G, head kvh * G + r % G).  Per 16-token page it forms
+//   S^T[t][r] = sum_d K[t][d] Q[r][d]       v_mfma_f32_16x16x32_bf16, D/32 steps
+//   O^T[d][r] += sum_t V^T[d][t] P^T[t][r]   v_mfma_f32_16x16x16_bf16, one per 16 output dims
+// The 16x16 accumulator layout (lane l holds column l % 16, rows 4*(l/16) .. +3) makes the score tile
+// the B operand of the P.V product: each lane softmaxes its own four scores, packs them to bf16 and
+// feeds them in, with no lane exchange.  The V^T operand wants four consecutive tokens of one dim per
+// lane, which dim-major V pages give with one 8-byte load.
+//
+// Pages stream through a ring of NBUF register buffers: the loads of page j + NBUF - 1 are issued
+// before page j is computed.  Buffers are indexed by compile-time constants (the loop is unrolled
+// NBUF times) and every issue is unconditional (past the last page it re-reads the last page), so the
+// compiler counts the loads in flight exactly and waits only for the page it is about to use.
+#pragma once
+
+#include "decode_args.h"
+#include "device_common.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <int D, int NT>
+struct WaveRows {
+  static constexpr int NK = D / 32;
+  int last[NT];          // last visible key position of this lane's row per N tile; -1: no row
+  int orow[NT];          // q row * H + head of this lane's row
+  bf16x8_t qB[NT][NK];   // B operands of the score product
+  int first_last;        // fewest visible keys among the rows (rows are in token order)
+};
+
+template <int D, int NT>
+struct WaveAcc {
+  static constexpr int ND = D / 16;
+  float m[NT];           // running max (log2 units), equal on the 4 lanes of a column
+  float lsum[NT];        // this lane's share of the exp-sum
+  float4_t acc[NT][ND];  // O^T: lane holds dims 16 t + 4 (l/16) + e of its column's row
+};
+
+// Rows [row0, row0 + 16 NT) of (sequence, kv head); `rows` = q_s * G of the sequence.
+template <int D, int NT>
+__device__ __forceinline__ void load_rows(const DecodeArgs &a, const SeqInfo &si, int kvh, int row0,
+                                          int rows, int col, int grp, WaveRows<D, NT> &w) {
+  const int G = a.group;
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int rr = row0 + n * 16 + col;
+    const int i = rr / G;
+    const int qrow = si.qbase + i;
+    const int head = kvh * G + (rr - i * G);
+    const bool ok = rr < rows && qrow < a.total_q;
+    w.last[n] = ok ? si.ctx - si.qs + i : -1;
+    w.orow[n] = qrow * a.num_heads + head;
+    const char *qp = static_cast<const char *>(a.q) + (int64_t)w.orow[n] * (D * 2);
+    #pragma unroll
+    for (int c = 0; c < WaveRows<D, NT>::NK; ++c) {
+      const uint4 v = ok ? ld16(qp + (4 * c + grp) * 16) : make_uint4(0, 0, 0, 0);
+      w.qB[n][c] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  w.first_last = si.ctx - si.qs + row0 / G;
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void init_acc(WaveAcc<D, NT> &s) {
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    s.m[n] = kNegBig;
+    s.lsum[n] = 0.f;
+    #pragma unroll
+    for (int t = 0; t < WaveAcc<D, NT>::ND; ++t) s.acc[n][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Attend the pages with logical block numbers blk_first + j * blk_stride, j < npages (npages <= 64),
+// of one sequence (block-table row bt_row) and one kv head.
+template <int D, int NT, int NBUF>
+__device__ __forceinline__ void attend_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
+                                             const int32_t *bt_row, int blk_first, int blk_stride,
+                                             int npages, int lane, const WaveRows<D, NT> &w,
+                                             WaveAcc<D, NT> &st) {
+  constexpr int ROWB = D * 2;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  if (npages <= 0) return;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int KVH = a.num_kv_heads;
+  const int64_t nb = a.num_blocks;
+  const int64_t page_bytes = (int64_t)kBlock * ROWB;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  const int ids = lane < npages ? bt_row[blk_first + lane * blk_stride] : 0;
+
+  uint4 kb[NBUF][NK];
+  uint2 vb[NBUF][ND];
+  bool okb[NBUF];
+  auto issue = [&](int j, uint4 *kr, uint2 *vr, bool &ok) {
+    const int bid = __builtin_amdgcn_readlane(ids, j);
+    ok = bid >= 0 && bid < nb;
+    const int64_t off = ((int64_t)(ok ? bid : 0) * KVH + kvh) * page_bytes;
+    const char *kp = kbase + off + col * ROWB + grp * 16;
+    #pragma unroll
+    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
+    const char *vp = vbase + off + (col * kBlock + 4 * grp) * 2;
+    #pragma unroll
+    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
+  };
+  auto compute = [&](int j, const uint4 *kr, uint2 *vr, bool ok) {
+    float4_t sc[NT];
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float4_t c4 = {0.f, 0.f, 0.f, 0.f};
+      #pragma unroll
+      for (int c = 0; c < NK; ++c)
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), w.qB[n][c], c4, 0, 0, 0);
+      sc[n] = c4 * a.scale_log2;
+    }
+    const int bstart = (blk_first + j * blk_stride) * kBlock;
+    if (!ok || bstart + kBlock > w.first_last + 1) {
+      // the page reaches past some row's last visible key (causal edge or context tail)
+      const int pos0 = bstart + 4 * grp;
+      #pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        #pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!ok || pos0 + e > w.last[n]) sc[n][e] = -INFINITY;
+      }
+      const int valid = ok ? si.ctx - bstart : 0;
+      if (valid < kBlock) {
+        // slots past the context may hold anything (even NaN): zero them so p = 0 adds exactly 0
+        #pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          if (4 * grp >= valid) vr[t].x = 0u;
+          else if (4 * grp + 1 >= valid) vr[t].x &= 0xffffu;
+          if (4 * grp + 2 >= valid) vr[t].y = 0u;
+          else if (4 * grp + 3 >= valid) vr[t].y &= 0xffffu;
+        }
+      }
+    }
+    // lazy running max: moves only when a score exceeds it by more than kRescaleSlack
+    bool need = false;
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float th = st.m[n] + kRescaleSlack;
+      need |= sc[n][0] > th || sc[n][1] > th || sc[n][2] > th || sc[n][3] > th;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      #pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float bm = fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3]));
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(st.m[n], bm);
+        const float alpha = exp2_hw(st.m[n] - mn);
+        st.m[n] = mn;
+        st.lsum[n] *= alpha;
+        #pragma unroll
+        for (int t = 0; t < ND; ++t) st.acc[n][t] *= alpha;
+      }
+    }
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float p0 = exp2_hw(sc[n][0] - st.m[n]);
+      const float p1 = exp2_hw(sc[n][1] - st.m[n]);
+      const float p2 = exp2_hw(sc[n][2] - st.m[n]);
+      const float p3 = exp2_hw(sc[n][3] - st.m[n]);
+      st.lsum[n] += (p0 + p1) + (p2 + p3);
+      const uint2 pw = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
+      const short4_t pB = __builtin_bit_cast(short4_t, pw);
+      #pragma unroll
+      for (int t = 0; t < ND; ++t)
+        st.acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vr[t]), pB,
+                                                                 st.acc[n][t], 0, 0, 0);
+    }
+  };
+
+  const int last_j = npages - 1;
+  #pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) issue(min(j, last_j), kb[j], vb[j], okb[j]);
+  int j0 = 0;
+  for (; j0 + NBUF <= npages; j0 += NBUF) {
+    #pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int bn = (b + NBUF - 1) % NBUF;   // a constant once the loop is unrolled
+      issue(min(j0 + b + NBUF - 1, last_j), kb[bn], vb[bn], okb[bn]);
+      compute(j0 + b, kb[b], vb[b], okb[b]);
+    }
+  }
+  // fewer than NBUF pages left: their loads are already in flight
+  #pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (j0 + b < npages) compute(j0 + b, kb[b], vb[b], okb[b]);
+}
+
+// Finish one wave's rows without other waves: fold the exp-sum over the column's 4 lanes and write
+// either the final output (bf16) + natural-log LSE, or the fp32 partial + log2 LSE of partition p.
+template <int D, int NT>
+__device__ __forceinline__ void finish_wave(const DecodeArgs &a, int p, bool single, int lane,
+                                            const WaveRows<D, NT> &w, const WaveAcc<D, NT> &st) {
+  constexpr int ND = D / 16;
+  const int grp = lane >> 4;
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float l = st.lsum[n];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (w.last[n] < 0) continue;
+    const bool seen = l > 0.f;
+    const float inv = seen ? 1.f / l : 0.f;
+    const float lse2 = seen ? st.m[n] + log2_hw(l) : -INFINITY;
+    const int64_t orow = w.orow[n];
+    if (single) {
+      uint16_t *o = static_cast<uint16_t *>(a.out) + orow * D + 4 * grp;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        const float4_t v = st.acc[n][t] * inv;
+        *reinterpret_cast<uint2 *>(o + t * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+      if (grp == 0 && a.lse) a.lse[orow] = lse2 * kLn2;
+    } else {
+      const int64_t prow = (int64_t)p * a.total_q * a.num_heads + orow;
+      float *o = a.part_o + prow * D + 4 * grp;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) *reinterpret_cast<float4_t *>(o + t * 16) = st.acc[n][t] * inv;
+      if (grp == 0) a.part_lse[prow] = lse2;
+    }
+  }
+}
+
+}  // namespace pkv

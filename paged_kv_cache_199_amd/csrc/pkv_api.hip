@@ -14,8 +14,12 @@ hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, v
 hipError_t launch_decode_valu(const DecodeArgs &a, bool bf16, int head_dim, int rows_per_tile,
                               hipStream_t st);
 int valu_max_rows(bool bf16);
-hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, int depth,
+                              bool persistent, int grid, hipStream_t st);
 int mfma_rows_per_tile(int rows);
+int mfma_default_depth(int head_dim, int rows_per_tile);
+int persistent_max_seqs();
+int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs);
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 }  // namespace pkv
@@ -23,6 +27,22 @@ hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStr
 namespace {
 
 constexpr int kBlockSize = 16;
+// A wave holds the page ids it visits in one register (64 lanes): a partition spans at most 64 pages
+// per wave of the 4-wave workgroup, or 64 pages in all when one wave attends a whole partition.
+constexpr int kMaxPartition = 64 * 4 * kBlockSize;
+constexpr int kMaxPartitionPersistent = 64 * kBlockSize;
+
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
@@ -36,6 +56,8 @@ struct Plan {
   int path;          // PKV_PATH_VALU / PKV_PATH_MFMA
   int rows_per_tile;
   int row_tiles;
+  int depth;         // pages of K/V per wave in the register ring (MFMA kernel)
+  int schedule;      // PKV_SCHEDULE_GRID / PKV_SCHEDULE_PERSISTENT
   int part_size;
   int num_parts;
   bool need_q_start;
@@ -54,6 +76,9 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
     if (opts->path != PKV_PATH_AUTO && opts->path != PKV_PATH_VALU && opts->path != PKV_PATH_MFMA)
       return PKV_ERR_UNSUPPORTED;
     if (opts->path == PKV_PATH_MFMA && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (opts->pipeline_depth != 0 && (opts->pipeline_depth < 2 || opts->pipeline_depth > 4))
+      return PKV_ERR_UNSUPPORTED;
+    if (opts->schedule < 0 || opts->schedule > PKV_SCHEDULE_PERSISTENT) return PKV_ERR_UNSUPPORTED;
   }
   return PKV_OK;
 }
@@ -81,6 +106,10 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   }
   pl.rows_per_tile = R;
   pl.row_tiles = ceil_div(rows, R);
+  pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth : pkv::mfma_default_depth(head_dim, R);
+  const int asked_sched = opts ? opts->schedule : 0;
+  const bool can_persist = pl.path == PKV_PATH_MFMA && num_seqs <= pkv::persistent_max_seqs();
+  pl.schedule = (asked_sched == PKV_SCHEDULE_GRID || !can_persist) ? PKV_SCHEDULE_GRID : PKV_SCHEDULE_PERSISTENT;
   int P = opts ? opts->partition_size : 0;
   if (P == 0) {
     const int64_t units1 = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
@@ -95,9 +124,11 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   }
   const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
   if (P >= whole) P = whole;
+  if (P > kMaxPartition) P = kMaxPartition;
+  if (pl.schedule == PKV_SCHEDULE_PERSISTENT && P > kMaxPartitionPersistent) P = kMaxPartitionPersistent;
   pl.part_size = P;
   pl.num_parts = ceil_div(max_context_len, P);
-  pl.need_q_start = ragged_q;
+  pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
   size_t off = 0;
   pl.off_q_start = off;
   if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
@@ -171,6 +202,8 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   info->path = pl.path;
   info->rows_per_tile = pl.rows_per_tile;
   info->row_tiles = pl.row_tiles;
+  info->pipeline_depth = pl.depth;
+  info->schedule = pl.schedule;
   info->workspace_bytes = pl.bytes;
   return PKV_OK;
 }
@@ -238,9 +271,14 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   if (opts && opts->event_main_begin &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_begin), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
-  const hipError_t le = pl.path == PKV_PATH_MFMA
-                           ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, s)
-                           : pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s);
+  int grid = 0;
+  if (pl.schedule == PKV_SCHEDULE_PERSISTENT)
+    grid = cu_count() * pkv::mfma_persistent_wgs_per_cu(head_dim, pl.rows_per_tile, pl.depth, num_seqs);
+  const hipError_t le =
+      pl.path == PKV_PATH_MFMA
+          ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, pl.depth,
+                                    pl.schedule == PKV_SCHEDULE_PERSISTENT, grid, s)
+          : pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s);
   if (le != hipSuccess) return PKV_ERR_LAUNCH;
   if (opts && opts->event_main_end &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_end), s) != hipSuccess)

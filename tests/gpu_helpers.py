@@ -23,7 +23,7 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def run_library(w: Workload, device, partition_size=0, path=_lib.PATH_AUTO, with_lse=True,
-                ragged=None, k_cache=None, v_cache=None):
+                ragged=None, k_cache=None, v_cache=None, schedule=0, depth=0):
     meta = w.device_meta(device)
     out = torch.empty_like(w.q)
     lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=device) if with_lse else None
@@ -33,7 +33,7 @@ def run_library(w: Workload, device, partition_size=0, path=_lib.PATH_AUTO, with
                            meta["block_tables"], meta["context_lens"], meta["q_lens"] if use_qlens else None,
                            out, lse, w.spec.num_heads, w.spec.num_kv_heads, w.spec.head_dim,
                            w.spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
-                           partition_size=partition_size, path=path)
+                           partition_size=partition_size, path=path, schedule=schedule, depth=depth)
     torch.cuda.synchronize()
     return out, lse
 

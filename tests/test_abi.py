@@ -61,20 +61,24 @@ def test_decode_argument_validation(lib):
     assert _decode(lib, **full, H=6, KVH=4) == -2               # H % KVH
     assert _decode(lib, **full, tq=5) == -2                     # total_q != S * max_q (q_lens NULL)
     assert _decode(lib, **full, mq=50) == -2                    # max_q_len > max_context_len
-    bad_p = _lib.DecodeOptions(24, 0, None, None)
+    bad_p = _lib.DecodeOptions(24, 0, 0, 0, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(bad_p)) == -3  # partition not a multiple of 16
-    bad_path = _lib.DecodeOptions(0, 9, None, None)
+    bad_path = _lib.DecodeOptions(0, 9, 0, 0, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(bad_path)) == -3
-    mfma_f32 = _lib.DecodeOptions(0, _lib.PATH_MFMA, None, None)
+    bad_depth = _lib.DecodeOptions(0, 0, 7, 0, None, None)
+    assert _decode(lib, **full, opts=ctypes.byref(bad_depth)) == -3
+    bad_sched = _lib.DecodeOptions(0, 0, 0, 5, None, None)
+    assert _decode(lib, **full, opts=ctypes.byref(bad_sched)) == -3
+    mfma_f32 = _lib.DecodeOptions(0, _lib.PATH_MFMA, 0, 0, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(mfma_f32)) == -3   # matrix-core path is bf16 only
     # a split launch needs workspace
-    small_p = _lib.DecodeOptions(16, 0, None, None)
+    small_p = _lib.DecodeOptions(16, 0, 0, 0, None, None)
     assert _decode(lib, **full, opts=ctypes.byref(small_p)) == -4
     assert _decode(lib, S=0) == 0                               # empty batch: no-op
 
 
 def test_workspace_and_partition_policy(lib):
-    o = _lib.DecodeOptions(0, 0, None, None)
+    o = _lib.DecodeOptions(0, 0, 0, 0, None, None)
     # long contexts split into 512-key partitions with fp32 partials
     info = _lib.DecodePlanInfo()
     assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o), ctypes.byref(info)) == 0
@@ -83,7 +87,7 @@ def test_workspace_and_partition_policy(lib):
     ws = lib.pkv_decode_workspace_bytes(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o))
     assert ws >= 64 * 256 * 64 * (128 + 1) * 4
     # a context that fits one partition needs no partials
-    o1 = _lib.DecodeOptions(4096, 0, None, None)
+    o1 = _lib.DecodeOptions(4096, 0, 0, 0, None, None)
     assert lib.pkv_decode_plan(4, 4, 1, 40, 4, 2, 64, 0, ctypes.byref(o1), ctypes.byref(info)) == 0
     assert info.partition_size == 48 and info.num_partitions == 1 and info.path == _lib.PATH_VALU
     assert lib.pkv_decode_workspace_bytes(4, 4, 1, 40, 4, 2, 64, 0, ctypes.byref(o1)) < 4096

@@ -21,19 +21,26 @@ def _say(*a):
     print(*a, flush=True)
 
 
+VALU = (_lib.PATH_VALU, _lib.SCHEDULE_AUTO)
+MFMA_GRID = (_lib.PATH_MFMA, _lib.SCHEDULE_GRID)
+MFMA_PERSIST = (_lib.PATH_MFMA, _lib.SCHEDULE_PERSISTENT)
+ALL_BF16 = [VALU, MFMA_GRID, MFMA_PERSIST]
+
+
 def _paths(w):
-    """Every kernel family that serves this dtype."""
-    return (_lib.PATH_VALU, _lib.PATH_MFMA) if w.spec.dtype == "bf16" else (_lib.PATH_VALU,)
+    """Every (kernel family, schedule) that serves this dtype."""
+    return ALL_BF16 if w.spec.dtype == "bf16" else [VALU]
 
 
 def _check_all(w, partition_size=0, strict=None):
-    for path in _paths(w):
-        _check_full(w, partition_size, path, strict)
+    for variant in _paths(w):
+        _check_full(w, partition_size, variant, strict)
 
 
-def _check_full(w, partition_size=0, path=_lib.PATH_AUTO, strict=None):
-    _say(f"[case] {w.spec.name} P={partition_size} path={path}")
-    out, lse = run_library(w, DEV, partition_size=partition_size, path=path)
+def _check_full(w, partition_size=0, variant=(_lib.PATH_AUTO, _lib.SCHEDULE_AUTO), strict=None):
+    path, sched = variant
+    _say(f"[case] {w.spec.name} P={partition_size} path={path} schedule={sched}")
+    out, lse = run_library(w, DEV, partition_size=partition_size, path=path, schedule=sched)
     ref_out, ref_lse = oracle_full(w)
     d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
     _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
@@ -70,7 +77,16 @@ def test_shared_prefix(gpu_lib, P):
 
 
 def test_spec_verify(gpu_lib):
-    _check_all(W.build(3, DEV))
+    w = W.build(3, DEV)
+    _check_all(w)
+    # every pipeline depth of the matrix-core kernel
+    for depth in (2, 4):
+        for variant in (MFMA_GRID, MFMA_PERSIST):
+            _say(f"[case] spec_verify depth={depth} {variant}")
+            out, lse = run_library(w, DEV, path=variant[0], schedule=variant[1], depth=depth)
+            ref_out, ref_lse = oracle_full(w)
+            d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+            assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
 
 def test_long_context_splitk_sampled(gpu_lib):
@@ -85,9 +101,9 @@ def test_long_context_splitk_sampled(gpu_lib):
     rows = np.zeros(w.total_q, dtype=bool)
     rows[seqs] = True
     _say(f"   seqs {seqs} ctx {[int(w.context_lens[s]) for s in seqs]}")
-    for path in _paths(w):
-        _say(f"[case] long_ctx_splitk_bf16 P=512 (full size) path={path}")
-        out, lse = run_library(w, DEV, partition_size=512, path=path)
+    for path, sched in _paths(w):
+        _say(f"[case] long_ctx_splitk_bf16 P=512 (full size) path={path} schedule={sched}")
+        out, lse = run_library(w, DEV, partition_size=512, path=path, schedule=sched)
         d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, rows=rows)
         _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
         assert d_out <= BF16_TOL and d_lse <= LSE_TOL
@@ -141,24 +157,25 @@ def test_poisoned_unread_slots_do_not_leak(gpu_lib):
             _check_all(w, P)
 
 
-@pytest.mark.parametrize("path", [_lib.PATH_VALU, _lib.PATH_MFMA])
-def test_repeat_is_bitwise_deterministic(gpu_lib, path):
+@pytest.mark.parametrize("variant", ALL_BF16)
+def test_repeat_is_bitwise_deterministic(gpu_lib, variant):
     w = W.build(3, DEV)
-    a, la = run_library(w, DEV, path=path)
-    b, lb = run_library(w, DEV, path=path)
+    a, la = run_library(w, DEV, path=variant[0], schedule=variant[1])
+    b, lb = run_library(w, DEV, path=variant[0], schedule=variant[1])
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
-@pytest.mark.parametrize("path", [_lib.PATH_VALU, _lib.PATH_MFMA])
-def test_physical_block_permutation_is_bitwise_invisible(gpu_lib, path):
+@pytest.mark.parametrize("variant", ALL_BF16)
+def test_physical_block_permutation_is_bitwise_invisible(gpu_lib, variant):
+    path, sched = variant
     w = W.build(1, DEV)
-    a, la = run_library(w, DEV, path=path)
+    a, la = run_library(w, DEV, path=path, schedule=sched)
     perm = np.random.default_rng(3).permutation(w.num_blocks)
     inv = torch.from_numpy(np.argsort(perm)).to(DEV)
     kc2 = w.k_cache.index_select(0, inv)          # kc2[perm[b]] = kc[b]
     vc2 = w.v_cache.index_select(0, inv)
     w.block_tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
-    b, lb = run_library(w, DEV, k_cache=kc2, v_cache=vc2, path=path)
+    b, lb = run_library(w, DEV, k_cache=kc2, v_cache=vc2, path=path, schedule=sched)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
