@@ -177,7 +177,7 @@ def main():
     if plan["path"] == _lib.PATH_MFMA:
         kernel = "decode_mfma_persistent_kernel" if plan["schedule"] == 2 else "decode_mfma_kernel"
     ws_bytes = plan["workspace_bytes"]
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = _lib.new_workspace(ws_bytes, dev)
     q_lens = None if w.uniform_q else meta["q_lens"]
     stream = torch.cuda.current_stream()
     total = args.warmup + args.steps

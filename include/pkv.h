@@ -67,7 +67,7 @@ typedef enum pkv_path { PKV_PATH_AUTO = 0, PKV_PATH_VALU = 1, PKV_PATH_MFMA = 2 
 /* How partition work maps onto the GPU (matrix-core kernel).  GRID: one workgroup per (kv head,
  * partition, sequence, row tile) of a grid sized from the host maxima.  PERSISTENT: a few workgroups
  * per CU whose waves walk the live partitions listed from context_lens (num_seqs <= 4096, partitions
- * of at most 1024 keys).  AUTO lets the library choose. */
+ * of a multiple of 64 and at most 1024 keys; ring depth 2 or 4).  AUTO lets the library choose. */
 typedef enum pkv_schedule {
   PKV_SCHEDULE_AUTO = 0, PKV_SCHEDULE_GRID = 1, PKV_SCHEDULE_PERSISTENT = 2
 } pkv_schedule;
@@ -76,7 +76,8 @@ typedef enum pkv_schedule {
  * struct also means defaults. */
 typedef struct pkv_decode_options {
   int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy;
-                               values above 4096 (1024 for the persistent schedule) are clamped */
+                               values above 4096 are clamped; the persistent schedule rounds up to
+                               a multiple of 64 and clamps to 1024 */
   int path;                 /* pkv_path */
   int pipeline_depth;       /* MFMA kernel: pages of K/V held per wave (2..4); 0 = policy */
   int schedule;             /* pkv_schedule */
@@ -109,6 +110,14 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int 
                                   int num_heads, int num_kv_heads, int head_dim, int dtype,
                                   const pkv_decode_options *opts);
 
+/*
+ * Zero the part of a decode workspace that must start at zero (the persistent schedule's claim
+ * counters).  Call it once after allocating a workspace, before its first use; every completed
+ * pkv_paged_attn_decode call leaves that part zero again, so later calls need no re-init (re-init
+ * after a call that failed on the device).  Enqueued on `stream` as a small kernel.
+ */
+int pkv_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
 /* What the library will launch for these sizes and options. */
 typedef struct pkv_decode_plan_info {
   int partition_size;      /* keys per partition */
@@ -132,7 +141,8 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
  * Preconditions on device data: 1 <= q_lens[s] <= context_lens[s] <= max_context_len,
  * context_lens[s] <= max_blocks_per_seq * block_size, block ids in [0, num_blocks), and
  * sum(q_lens) == total_q (q_lens == NULL: total_q == num_seqs * max_q_len).
- * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0).
+ * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0) and must
+ * have been through pkv_decode_workspace_init() once (or be zero-filled by the caller).
  * `scale` multiplies the raw dot products (usually 1/sqrt(head_dim)).
  */
 int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,

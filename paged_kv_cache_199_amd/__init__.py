@@ -3,7 +3,7 @@
     from paged_kv_cache_199_amd import kv_cache_write, paged_attn_decode
 """
 from ._lib import (PATH_AUTO, PATH_MFMA, PATH_VALU, decode_plan, decode_workspace_bytes,
-                   kv_cache_write, load, paged_attn_decode)
+                   kv_cache_write, load, new_workspace, paged_attn_decode)
 
 __all__ = ["kv_cache_write", "paged_attn_decode", "decode_workspace_bytes", "decode_plan",
-           "load", "PATH_AUTO", "PATH_VALU", "PATH_MFMA"]
+           "load", "new_workspace", "PATH_AUTO", "PATH_VALU", "PATH_MFMA"]

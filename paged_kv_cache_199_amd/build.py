@@ -22,6 +22,8 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the softmax rescale then needs no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

@@ -85,6 +85,17 @@ __global__ __launch_bounds__(1024) void q_start_kernel(const int32_t *q_lens, in
   if (tid == 1023) q_start[n] = part[1023];
 }
 
+// Byte fill to zero with vector stores (a kernel, not hipMemsetAsync, so it is safe in captured graphs).
+__global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
+  const size_t blocks = (bytes + 255) / 256;
+  zero_kernel<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(static_cast<unsigned char *>(p), bytes);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st) {
   const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * a.num_heads;
   const int grid = (int)((waves + 3) / 4);

@@ -11,11 +11,13 @@
 //    the host-known maxima; workgroups past a sequence's end exit at once.  The waves of a workgroup
 //    take every fourth page of the partition and merge through LDS.
 //  * persistent: a grid of a few workgroups per CU.  Every workgroup lists the live work items from
-//    context_lens into LDS (items are (kv head, sequence, partition, row tile), kv-head-major), the
+//    context_lens into LDS (items are (kv head, sequence, row tile, partition), kv-head-major), the
 //    8 XCDs take equal contiguous shares of the list, and every wave is an independent worker that
-//    takes every W-th item of its XCD's share and attends the whole partition itself.  No workgroup
-//    is spent on an empty partition, ragged lengths spread evenly over all waves, and the items that
-//    read one kv head's pages (including prefix pages several sequences share) stay under one L2.
+//    takes an equal contiguous share of its XCD's items.  Consecutive partitions of one sequence in
+//    that share form one page stream (the softmax state is flushed at each partition boundary), so
+//    the page pipeline restarts only when the sequence changes.  No workgroup is spent on an empty
+//    partition, ragged lengths spread evenly over all waves, and the items that read one kv head's
+//    pages (including prefix pages several sequences share) stay under one L2.
 #include "mfma_wave.h"
 
 namespace pkv {
@@ -179,9 +181,15 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
   const int xcd = blockIdx.x & 7;
   const int n_wg = (int)((gridDim.x - xcd + 7) >> 3);
   const int64_t lo = L * xcd / 8;
-  const int64_t hi = L * (xcd + 1) / 8;
+  const int64_t span = L * (xcd + 1) / 8 - lo;
   const int W = n_wg * 4;
-  for (int64_t k = lo + (blockIdx.x >> 3) * 4 + wave; k < hi; k += W) {
+  const int wx = (blockIdx.x >> 3) * 4 + wave;
+  const int64_t k_end = lo + span * (wx + 1) / W;
+  const int PP = a.part_size / kBlock;
+  int64_t k = lo + span * wx / W;
+  // Items are ordered (kv head, sequence, row tile, partition): the wave's contiguous share walks
+  // runs of consecutive partitions of one (sequence, kv head, row tile) as one page stream.
+  while (k < k_end) {
     const int kvh = (int)(k / I);
     const int r = (int)(k - (int64_t)kvh * I);
     int s0 = 0, s1 = S;                              // pre[s0] <= r < pre[s1]
@@ -190,58 +198,60 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
       if (pre[mid] <= r) s0 = mid;
       else s1 = mid;
     }
-    const int s = s0;
-    const int local = r - pre[s];
-    const int rts = trts[s];
-    const int p = local / rts;
-    const int rt = local - p * rts;
+    // LDS reads come back in vector registers; the values are wave-uniform, and saying so keeps the
+    // block-table row pointer scalar (its page ids then come through the scalar cache)
+    const int s = __builtin_amdgcn_readfirstlane(s0);
     SeqInfo si;
-    si.ctx = tctx[s];
-    si.qs = tqs[s];
-    si.qbase = tqb[s];
+    si.ctx = __builtin_amdgcn_readfirstlane(tctx[s]);
+    si.qs = __builtin_amdgcn_readfirstlane(tqs[s]);
+    si.qbase = __builtin_amdgcn_readfirstlane(tqb[s]);
     si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
+    const int local = __builtin_amdgcn_readfirstlane(r - pre[s]);
+    const int rt = local / si.nparts;
+    const int p = local - rt * si.nparts;
+    const int m = (int)min((int64_t)(si.nparts - p), k_end - k);
+    const int nblk = (si.ctx + kBlock - 1) / kBlock;
 
     WaveRows<D, NT> w;
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
     WaveAcc<D, NT> st;
     init_acc<D, NT>(st);
-    const int tok0 = p * a.part_size;
-    const int tok1 = min(si.ctx, tok0 + a.part_size);
-    const int npages = (tok1 - tok0 + kBlock - 1) / kBlock;
-    attend_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq,
-                              tok0 / kBlock, 1, npages, lane, w, st);
-    finish_wave<D, NT>(a, p, si.nparts == 1, lane, w, st);
+    const bool single = si.nparts == 1;
+    stream_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq, p * PP,
+                              min((p + m) * PP, nblk), PP, lane, w, st, [&](int part) {
+                                finish_wave<D, NT>(a, part, single, lane, w, st);
+                                init_acc<D, NT>(st);
+                              });
+    k += m;
   }
 }
 
 // Rows one launch covers per work item: 16 per N tile, at most two N tiles.
 int mfma_rows_per_tile(int rows) { return rows > 16 ? 32 : 16; }
 
-// Pages in flight per wave = depth - 1.  Depths 2..4 are built.
-int mfma_default_depth(int head_dim, int rows_per_tile) { return 3; }
+// Pages in flight per wave = depth - 1.  Depths 2..4 are built for the grid schedule; the persistent
+// schedule streams runs of partitions and takes depths that divide the pages of a partition (2, 4).
+int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent) { return persistent ? 4 : 3; }
 
 // Largest batch the persistent schedule lists in LDS, and the LDS it needs.
 int persistent_max_seqs() { return 4096; }
 size_t persistent_lds_bytes(int num_seqs) { return (size_t)(5 * num_seqs + 1) * sizeof(int); }
 
-template <int D, int NT, int NBUF>
-static hipError_t launch_one(const DecodeArgs &a, bool persistent, int grid, hipStream_t st) {
-  if (persistent) {
-    decode_mfma_persistent_kernel<D, NT, NBUF><<<grid, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
-  } else {
-    decode_mfma_kernel<D, NT, NBUF><<<a.per_xcd * 8, 256, 0, st>>>(a);
-  }
-  return hipGetLastError();
-}
-
 template <int D, int NT>
 static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent, int grid,
                                  hipStream_t st) {
-  switch (depth) {
-    case 2: return launch_one<D, NT, 2>(a, persistent, grid, st);
-    case 4: return launch_one<D, NT, 4>(a, persistent, grid, st);
-    default: return launch_one<D, NT, 3>(a, persistent, grid, st);
+  if (persistent) {
+    const int g = grid;
+    if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2><<<g, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
+    else decode_mfma_persistent_kernel<D, NT, 4><<<g, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
+    return hipGetLastError();
   }
+  switch (depth) {
+    case 2: decode_mfma_kernel<D, NT, 2><<<a.per_xcd * 8, 256, 0, st>>>(a); break;
+    case 4: decode_mfma_kernel<D, NT, 4><<<a.per_xcd * 8, 256, 0, st>>>(a); break;
+    default: decode_mfma_kernel<D, NT, 3><<<a.per_xcd * 8, 256, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
 }
 
 // Workgroups of one persistent-kernel instance that fit a CU at once.
@@ -256,11 +266,7 @@ static int occupancy_of(int num_seqs) {
 
 template <int D, int NT>
 static int occupancy_dn(int depth, int num_seqs) {
-  switch (depth) {
-    case 2: return occupancy_of<D, NT, 2>(num_seqs);
-    case 4: return occupancy_of<D, NT, 4>(num_seqs);
-    default: return occupancy_of<D, NT, 3>(num_seqs);
-  }
+  return depth == 2 ? occupancy_of<D, NT, 2>(num_seqs) : occupancy_of<D, NT, 4>(num_seqs);
 }
 
 // Cached per (head_dim, N tiles, depth) and per LDS size class (the tables grow with the batch).

@@ -81,6 +81,81 @@ __device__ __forceinline__ void init_acc(WaveAcc<D, NT> &s) {
   }
 }
 
+// One 16-token page starting at logical position bstart: scores, mask, online softmax, P.V.
+template <int D, int NT>
+__device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si, int bstart,
+                                          const uint4 *kr, uint2 *vr, bool ok, int lane,
+                                          const WaveRows<D, NT> &w, WaveAcc<D, NT> &st) {
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int grp = lane >> 4;
+  float4_t sc[NT];
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float4_t c4 = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int c = 0; c < NK; ++c)
+      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), w.qB[n][c], c4, 0, 0, 0);
+    sc[n] = c4 * a.scale_log2;
+  }
+  if (!ok || bstart + kBlock > w.first_last + 1) {
+    // the page reaches past some row's last visible key (causal edge or context tail)
+    const int pos0 = bstart + 4 * grp;
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      #pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!ok || pos0 + e > w.last[n]) sc[n][e] = -INFINITY;
+    }
+    const int valid = ok ? si.ctx - bstart : 0;
+    if (valid < kBlock) {
+      // slots past the context may hold anything (even NaN): zero them so p = 0 adds exactly 0
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        if (4 * grp >= valid) vr[t].x = 0u;
+        else if (4 * grp + 1 >= valid) vr[t].x &= 0xffffu;
+        if (4 * grp + 2 >= valid) vr[t].y = 0u;
+        else if (4 * grp + 3 >= valid) vr[t].y &= 0xffffu;
+      }
+    }
+  }
+  // lazy running max: moves only when a score exceeds it by more than kRescaleSlack
+  bool need = false;
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float th = st.m[n] + kRescaleSlack;
+    need |= sc[n][0] > th || sc[n][1] > th || sc[n][2] > th || sc[n][3] > th;
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float bm = fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(st.m[n], bm);
+      const float alpha = exp2_hw(st.m[n] - mn);
+      st.m[n] = mn;
+      st.lsum[n] *= alpha;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) st.acc[n][t] *= alpha;
+    }
+  }
+  #pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float p0 = exp2_hw(sc[n][0] - st.m[n]);
+    const float p1 = exp2_hw(sc[n][1] - st.m[n]);
+    const float p2 = exp2_hw(sc[n][2] - st.m[n]);
+    const float p3 = exp2_hw(sc[n][3] - st.m[n]);
+    st.lsum[n] += (p0 + p1) + (p2 + p3);
+    const uint2 pw = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
+    const short4_t pB = __builtin_bit_cast(short4_t, pw);
+    #pragma unroll
+    for (int t = 0; t < ND; ++t)
+      st.acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vr[t]), pB,
+                                                               st.acc[n][t], 0, 0, 0);
+  }
+}
+
 // Attend the pages with logical block numbers blk_first + j * blk_stride, j < npages (npages <= 64),
 // of one sequence (block-table row bt_row) and one kv head.
 template <int D, int NT, int NBUF>
@@ -116,72 +191,7 @@ __device__ __forceinline__ void attend_pages(const DecodeArgs &a, const SeqInfo 
     for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
   };
   auto compute = [&](int j, const uint4 *kr, uint2 *vr, bool ok) {
-    float4_t sc[NT];
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float4_t c4 = {0.f, 0.f, 0.f, 0.f};
-      #pragma unroll
-      for (int c = 0; c < NK; ++c)
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), w.qB[n][c], c4, 0, 0, 0);
-      sc[n] = c4 * a.scale_log2;
-    }
-    const int bstart = (blk_first + j * blk_stride) * kBlock;
-    if (!ok || bstart + kBlock > w.first_last + 1) {
-      // the page reaches past some row's last visible key (causal edge or context tail)
-      const int pos0 = bstart + 4 * grp;
-      #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!ok || pos0 + e > w.last[n]) sc[n][e] = -INFINITY;
-      }
-      const int valid = ok ? si.ctx - bstart : 0;
-      if (valid < kBlock) {
-        // slots past the context may hold anything (even NaN): zero them so p = 0 adds exactly 0
-        #pragma unroll
-        for (int t = 0; t < ND; ++t) {
-          if (4 * grp >= valid) vr[t].x = 0u;
-          else if (4 * grp + 1 >= valid) vr[t].x &= 0xffffu;
-          if (4 * grp + 2 >= valid) vr[t].y = 0u;
-          else if (4 * grp + 3 >= valid) vr[t].y &= 0xffffu;
-        }
-      }
-    }
-    // lazy running max: moves only when a score exceeds it by more than kRescaleSlack
-    bool need = false;
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float th = st.m[n] + kRescaleSlack;
-      need |= sc[n][0] > th || sc[n][1] > th || sc[n][2] > th || sc[n][3] > th;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float bm = fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3]));
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(st.m[n], bm);
-        const float alpha = exp2_hw(st.m[n] - mn);
-        st.m[n] = mn;
-        st.lsum[n] *= alpha;
-        #pragma unroll
-        for (int t = 0; t < ND; ++t) st.acc[n][t] *= alpha;
-      }
-    }
-    #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const float p0 = exp2_hw(sc[n][0] - st.m[n]);
-      const float p1 = exp2_hw(sc[n][1] - st.m[n]);
-      const float p2 = exp2_hw(sc[n][2] - st.m[n]);
-      const float p3 = exp2_hw(sc[n][3] - st.m[n]);
-      st.lsum[n] += (p0 + p1) + (p2 + p3);
-      const uint2 pw = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
-      const short4_t pB = __builtin_bit_cast(short4_t, pw);
-      #pragma unroll
-      for (int t = 0; t < ND; ++t)
-        st.acc[n][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, vr[t]), pB,
-                                                                 st.acc[n][t], 0, 0, 0);
-    }
+    mfma_page<D, NT>(a, si, (blk_first + j * blk_stride) * kBlock, kr, vr, ok, lane, w, st);
   };
 
   const int last_j = npages - 1;
@@ -200,6 +210,75 @@ __device__ __forceinline__ void attend_pages(const DecodeArgs &a, const SeqInfo 
   #pragma unroll
   for (int b = 0; b < NBUF - 1; ++b)
     if (j0 + b < npages) compute(j0 + b, kb[b], vb[b], okb[b]);
+}
+
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// Attend the consecutive logical pages [jb, je) of one (sequence, kv head, row tile), flushing the
+// softmax state through flush(partition) after the last page of every partition of PP pages and
+// after page je - 1.  jb and PP are multiples of NBUF, so partition ends fall on the last page of a
+// ring cycle and the flush sits outside the unrolled cycle.  Page ids come through the scalar cache
+// (the block table is read-only here): the id of the page issued NBUF steps later is fetched while
+// the current page is computed, so those loads never hold up the vector loads and a run of any
+// length streams without a restart.
+template <int D, int NT, int NBUF, class Flush>
+__device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
+                                             const int32_t *bt_row, int jb, int je, int PP, int lane,
+                                             const WaveRows<D, NT> &w, WaveAcc<D, NT> &st,
+                                             Flush flush) {
+  constexpr int ROWB = D * 2;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int n = je - jb;
+  if (n <= 0) return;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int KVH = a.num_kv_heads;
+  const int64_t nb = a.num_blocks;
+  const int64_t page_bytes = (int64_t)kBlock * ROWB;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  const_i32 *btc = (const_i32 *)(bt_row);   // a C-style cast is the only way into address space 4
+  const int last = je - 1;
+  auto id_of = [&](int j) -> int { return btc[__builtin_amdgcn_readfirstlane(min(j, last))]; };
+
+  uint4 kb[NBUF][NK];
+  uint2 vb[NBUF][ND];
+  bool okb[NBUF];
+  auto issue = [&](int bid, uint4 *kr, uint2 *vr, bool &ok) {
+    ok = bid >= 0 && bid < nb;
+    const int64_t off = ((int64_t)(ok ? bid : 0) * KVH + kvh) * page_bytes;
+    const char *kp = kbase + off + col * ROWB + grp * 16;
+    #pragma unroll
+    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
+    const char *vp = vbase + off + (col * kBlock + 4 * grp) * 2;
+    #pragma unroll
+    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
+  };
+
+  int sid[NBUF];
+  #pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) issue(id_of(jb + j), kb[j], vb[j], okb[j]);
+  #pragma unroll
+  for (int b = 0; b < NBUF; ++b) sid[b] = id_of(jb + NBUF - 1 + b);
+  int j0 = 0;
+  for (; j0 + NBUF <= n; j0 += NBUF) {
+    #pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int bn = (b + NBUF - 1) % NBUF;   // constants once the loop is unrolled
+      issue(sid[b], kb[bn], vb[bn], okb[bn]);
+      sid[b] = id_of(jb + j0 + b + 2 * NBUF - 1);
+      mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
+    }
+    const int jl = jb + j0 + NBUF - 1;
+    if ((jl + 1) % PP == 0 || jl == last) flush(jl / PP);
+  }
+  if (j0 < n) {
+    #pragma unroll
+    for (int b = 0; b < NBUF - 1; ++b)
+      if (j0 + b < n) mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
+    flush(last / PP);
+  }
 }
 
 // Finish one wave's rows without other waves: fold the exp-sum over the column's 4 lanes and write

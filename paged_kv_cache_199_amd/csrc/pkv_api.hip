@@ -17,11 +17,12 @@ int valu_max_rows(bool bf16);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, int depth,
                               bool persistent, int grid, hipStream_t st);
 int mfma_rows_per_tile(int rows);
-int mfma_default_depth(int head_dim, int rows_per_tile);
+int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent);
 int persistent_max_seqs();
 int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs);
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 }  // namespace pkv
 
 namespace {
@@ -30,7 +31,7 @@ constexpr int kBlockSize = 16;
 // A wave holds the page ids it visits in one register (64 lanes): a partition spans at most 64 pages
 // per wave of the 4-wave workgroup, or 64 pages in all when one wave attends a whole partition.
 constexpr int kMaxPartition = 64 * 4 * kBlockSize;
-constexpr int kMaxPartitionPersistent = 64 * kBlockSize;
+constexpr int kMaxPartitionPersistent = 64 * kBlockSize;   // keeps the item count per sequence small
 
 int cu_count() {
   static int cached[64];
@@ -61,7 +62,7 @@ struct Plan {
   int part_size;
   int num_parts;
   bool need_q_start;
-  size_t off_q_start, off_part_lse, off_part_o, bytes;
+  size_t off_counters, off_q_start, off_part_lse, off_part_o, bytes;
 };
 
 int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
@@ -106,10 +107,13 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   }
   pl.rows_per_tile = R;
   pl.row_tiles = ceil_div(rows, R);
-  pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth : pkv::mfma_default_depth(head_dim, R);
   const int asked_sched = opts ? opts->schedule : 0;
   const bool can_persist = pl.path == PKV_PATH_MFMA && num_seqs <= pkv::persistent_max_seqs();
   pl.schedule = (asked_sched == PKV_SCHEDULE_GRID || !can_persist) ? PKV_SCHEDULE_GRID : PKV_SCHEDULE_PERSISTENT;
+  const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
+  pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth
+                                            : pkv::mfma_default_depth(head_dim, R, persist);
+  if (persist && pl.depth == 3) pl.depth = 4;   // the persistent ring depth must divide 4
   int P = opts ? opts->partition_size : 0;
   if (P == 0) {
     const int64_t units1 = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
@@ -125,11 +129,17 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
   if (P >= whole) P = whole;
   if (P > kMaxPartition) P = kMaxPartition;
-  if (pl.schedule == PKV_SCHEDULE_PERSISTENT && P > kMaxPartitionPersistent) P = kMaxPartitionPersistent;
+  if (persist) {
+    // whole ring cycles per partition: a multiple of 64 keys (4 pages), at most 1024
+    P = ceil_div(P, 4 * kBlockSize) * 4 * kBlockSize;
+    if (P > kMaxPartitionPersistent) P = kMaxPartitionPersistent;
+  }
   pl.part_size = P;
   pl.num_parts = ceil_div(max_context_len, P);
   pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
   size_t off = 0;
+  pl.off_counters = off;
+  if (persist) off = align_up(off + pkv::kCounterRegion);
   pl.off_q_start = off;
   if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
   pl.off_part_lse = off;
@@ -159,6 +169,14 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
+}
+
+int pkv_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+  if (workspace_bytes == 0) return PKV_OK;
+  if (!workspace) return PKV_ERR_NULL;
+  const size_t n = workspace_bytes < (size_t)pkv::kCounterRegion ? workspace_bytes : (size_t)pkv::kCounterRegion;
+  return pkv::launch_zero(workspace, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                         : PKV_ERR_LAUNCH;
 }
 
 int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
@@ -246,6 +264,8 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   a.lse = lse;
   a.part_lse = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
   a.part_o = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
+  a.counters = pl.schedule == PKV_SCHEDULE_PERSISTENT ? reinterpret_cast<unsigned *>(ws + pl.off_counters)
+                                                      : nullptr;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.max_blocks_per_seq = max_blocks_per_seq;

@@ -195,3 +195,25 @@ def test_write_skips_negative_and_out_of_range_slots(gpu_lib):
     keep = np.where(slots < nslots, slots, -1)
     want_k, want_v = O.kv_cache_write(kc0, vc0, host_bits(k), host_bits(v), keep)
     assert np.array_equal(host_bits(w.k_cache), want_k) and np.array_equal(host_bits(w.v_cache), want_v)
+
+
+def test_workspace_reuse_across_calls(gpu_lib):
+    """The persistent schedule's claim counters return to zero after every call, so one workspace
+    serves many calls (here: three different workloads and sizes, twice each)."""
+    ws = _lib.new_workspace(64 << 20, DEV)
+    for idx in (3, 1, 2, 3, 1, 2):
+        w = W.build(idx, DEV)
+        meta = w.device_meta(DEV)
+        out = torch.empty_like(w.q)
+        lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=DEV)
+        _lib.paged_attn_decode(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"], None,
+                               out, lse, w.spec.num_heads, w.spec.num_kv_heads, w.spec.head_dim, 16, w.scale,
+                               w.max_context_len, max_q_len=w.max_q_len, path=_lib.PATH_MFMA,
+                               schedule=_lib.SCHEDULE_PERSISTENT, workspace=ws)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle_full(w)
+        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+        _say(f"[case] workspace reuse {w.spec.name}: {d_out:.3e} {d_lse:.3e}")
+        assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+    head = ws[:256].cpu()
+    assert int(head.sum()) == 0, "claim counters were not reset"
