@@ -110,14 +110,6 @@ size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int 
                                   int num_heads, int num_kv_heads, int head_dim, int dtype,
                                   const pkv_decode_options *opts);
 
-/*
- * Zero the part of a decode workspace that must start at zero (the persistent schedule's claim
- * counters).  Call it once after allocating a workspace, before its first use; every completed
- * pkv_paged_attn_decode call leaves that part zero again, so later calls need no re-init (re-init
- * after a call that failed on the device).  Enqueued on `stream` as a small kernel.
- */
-int pkv_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
-
 /* What the library will launch for these sizes and options. */
 typedef struct pkv_decode_plan_info {
   int partition_size;      /* keys per partition */
@@ -141,8 +133,8 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
  * Preconditions on device data: 1 <= q_lens[s] <= context_lens[s] <= max_context_len,
  * context_lens[s] <= max_blocks_per_seq * block_size, block ids in [0, num_blocks), and
  * sum(q_lens) == total_q (q_lens == NULL: total_q == num_seqs * max_q_len).
- * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0) and must
- * have been through pkv_decode_workspace_init() once (or be zero-filled by the caller).
+ * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0); its contents
+ * on entry do not matter.
  * `scale` multiplies the raw dot products (usually 1/sqrt(head_dim)).
  */
 int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,

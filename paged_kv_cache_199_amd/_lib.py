@@ -44,7 +44,6 @@ EXPORTS = {
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                        _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                        ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
-    "pkv_decode_workspace_init": (_c_int, [_vp, _c_sz, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_version": (_c_int, []),
 }
@@ -130,11 +129,9 @@ def decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_he
                                                  num_kv_heads, head_dim, dtype_code, ctypes.byref(o)))
 
 
-def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
-    """A decode workspace of nbytes on `device`, initialised for its first use."""
-    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
-    _check(load().pkv_decode_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "pkv_decode_workspace_init")
-    return ws
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A decode workspace of nbytes on `device` (contents on entry do not matter)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
@@ -160,8 +157,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     q_lens None means every sequence has max_q_len new tokens.  max_context_len is a host-known upper
     bound of context_lens (the kernels never read device data on the host).  A workspace tensor
     (any dtype, contiguous, on the GPU) of at least decode_workspace_bytes() bytes is allocated when
-    not given (and initialised); a caller-supplied workspace must come from new_workspace() or have
-    been through pkv_decode_workspace_init once.  `events` = (begin, end) torch.cuda.Event pair that has been recorded once: the library
+    not given.  `events` = (begin, end) torch.cuda.Event pair that has been recorded once: the library
     records them around its partition kernel."""
     lib = load()
     _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
@@ -186,7 +182,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                               num_kv_heads, head_dim, code, ctypes.byref(o)))
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device, stream)
+        workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                    _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),

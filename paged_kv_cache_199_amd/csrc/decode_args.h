@@ -18,7 +18,6 @@ struct DecodeArgs {
   float *lse;                  // may be NULL
   float *part_o;               // [num_parts][total_q][H][D] fp32, NULL when num_parts == 1
   float *part_lse;             // [num_parts][total_q][H], log2 units
-  unsigned *counters;          // persistent schedule: claim counters (zero before and after a call)
   int64_t num_blocks;
   int num_seqs;
   int max_blocks_per_seq;
@@ -35,11 +34,6 @@ struct DecodeArgs {
   int units;                   // num_kv_heads * num_parts * num_seqs * row_tiles
   int per_xcd;                 // ceil(units / 8)
 };
-
-// Claim counters of the persistent schedule, one 64-byte line each: [0, 8) per-XCD item counters,
-// [8] waves that have finished.  The last wave to finish puts every counter back to zero.
-constexpr int kCounterStride = 16;        // in unsigned
-constexpr int kCounterRegion = 9 * kCounterStride * 4;
 
 // Per-unit sequence facts with the clamps that keep bad metadata memory-safe.
 struct SeqInfo {

@@ -3,13 +3,17 @@
 // The lfm25-inference page ("Runtime Design") decodes long contexts with a split-K reduction.  Each
 // partition p of a row leaves a softmax over its own keys, o_p, and its log-sum-exp, lse_p.  The
 // merged row is  out = sum_p w_p o_p / sum_p w_p  with  w_p = exp(lse_p - max_p lse_p), and
-// lse = max + log(sum_p w_p); a partition in which the row saw no key has lse_p = -inf and weight 0.
+// lse = max + log(sum_p w_p); a partition in which the row saw no key has lse_p = -inf and weight 0
+// (exp2 of -inf is 0, so it needs no special case).
 #include "decode_args.h"
 #include "device_common.h"
 
 namespace pkv {
 
-// One wave per (sequence, new token, head); partitions in log2 units.
+// One wave per (sequence, new token, head); partition LSEs are in log2 units.  The LSEs of up to 64
+// partitions are read at once (one per lane), their max and weight sum are wave reductions, and the
+// weights are broadcast from the lane that holds them, so the partial outputs stream with several
+// loads in flight instead of one dependent load per partition.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int DPL = D / 64;
@@ -29,23 +33,42 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int64_t stride = (int64_t)a.total_q * H;          // between partitions
   const int64_t base = (int64_t)row * H + h;
 
+  float acc[DPL];
+  #pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
   float M = -INFINITY;
   for (int p = lane; p < si.nparts; p += 64) M = fmaxf(M, a.part_lse[p * stride + base]);
   M = wave_max(M);
   const float Ms = M == -INFINITY ? 0.f : M;
   float L = 0.f;
-  for (int p = lane; p < si.nparts; p += 64) L += exp2_hw(a.part_lse[p * stride + base] - Ms);
-  L = wave_sum(L);
-
-  float acc[DPL];
-  #pragma unroll
-  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-  for (int p = 0; p < si.nparts; ++p) {
-    const float w = exp2_hw(a.part_lse[p * stride + base] - Ms);
-    const float *op = a.part_o + (p * stride + base) * D;
-    #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] = fmaf(w, op[lane + 64 * k], acc[k]);
+  for (int c0 = 0; c0 < si.nparts; c0 += 64) {
+    const int pl = c0 + lane;
+    const float wl = pl < si.nparts ? exp2_hw(a.part_lse[pl * stride + base] - Ms) : 0.f;
+    L += wl;
+    const int n = min(64, si.nparts - c0);
+    const float *op = a.part_o + (c0 * stride + base) * D + lane;
+    int j = 0;
+    for (; j + 8 <= n; j += 8) {
+      float v[8][DPL];
+      #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        #pragma unroll
+        for (int k = 0; k < DPL; ++k) v[u][k] = op[(j + u) * stride * D + 64 * k];
+      }
+      #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wp = __shfl(wl, j + u);
+        #pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, v[u][k], acc[k]);
+      }
+    }
+    for (; j < n; ++j) {
+      const float wp = __shfl(wl, j);
+      #pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, op[j * stride * D + 64 * k], acc[k]);
+    }
   }
+  L = wave_sum(L);
   const bool seen = L > 0.f;
   const float inv = seen ? 1.f / L : 0.f;
   #pragma unroll
@@ -83,17 +106,6 @@ __global__ __launch_bounds__(1024) void q_start_kernel(const int32_t *q_lens, in
     run += max(q_lens[k], 0);
   }
   if (tid == 1023) q_start[n] = part[1023];
-}
-
-// Byte fill to zero with vector stores (a kernel, not hipMemsetAsync, so it is safe in captured graphs).
-__global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
-}
-
-hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
-  const size_t blocks = (bytes + 255) / 256;
-  zero_kernel<<<(unsigned)(blocks < 1024 ? blocks : 1024), 256, 0, st>>>(static_cast<unsigned char *>(p), bytes);
-  return hipGetLastError();
 }
 
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st) {

@@ -22,7 +22,6 @@ int persistent_max_seqs();
 int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs);
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
-hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 }  // namespace pkv
 
 namespace {
@@ -62,7 +61,7 @@ struct Plan {
   int part_size;
   int num_parts;
   bool need_q_start;
-  size_t off_counters, off_q_start, off_part_lse, off_part_o, bytes;
+  size_t off_q_start, off_part_lse, off_part_o, bytes;
 };
 
 int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
@@ -138,8 +137,6 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   pl.num_parts = ceil_div(max_context_len, P);
   pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
   size_t off = 0;
-  pl.off_counters = off;
-  if (persist) off = align_up(off + pkv::kCounterRegion);
   pl.off_q_start = off;
   if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
   pl.off_part_lse = off;
@@ -169,14 +166,6 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
-}
-
-int pkv_decode_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
-  if (workspace_bytes == 0) return PKV_OK;
-  if (!workspace) return PKV_ERR_NULL;
-  const size_t n = workspace_bytes < (size_t)pkv::kCounterRegion ? workspace_bytes : (size_t)pkv::kCounterRegion;
-  return pkv::launch_zero(workspace, n, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
-                                                                                         : PKV_ERR_LAUNCH;
 }
 
 int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
@@ -264,8 +253,6 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   a.lse = lse;
   a.part_lse = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
   a.part_o = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
-  a.counters = pl.schedule == PKV_SCHEDULE_PERSISTENT ? reinterpret_cast<unsigned *>(ws + pl.off_counters)
-                                                      : nullptr;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.max_blocks_per_seq = max_blocks_per_seq;

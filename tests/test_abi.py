@@ -97,11 +97,6 @@ def test_workspace_and_partition_policy(lib):
     assert info.rows_per_tile == 32 and info.row_tiles == 1
 
 
-def test_workspace_init_validation(lib):
-    assert lib.pkv_decode_workspace_init(None, 0, None) == 0
-    assert lib.pkv_decode_workspace_init(None, 256, None) == -1
-
-
 def test_write_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
     assert lib.pkv_kv_cache_write(None, f, f, f, f, 3, 8, 2, 128, 16, 1, None) == -1

@@ -198,8 +198,8 @@ def test_write_skips_negative_and_out_of_range_slots(gpu_lib):
 
 
 def test_workspace_reuse_across_calls(gpu_lib):
-    """The persistent schedule's claim counters return to zero after every call, so one workspace
-    serves many calls (here: three different workloads and sizes, twice each)."""
+    """One workspace serves many calls of different shapes (three workloads, twice each): no call
+    depends on what an earlier call left in it."""
     ws = _lib.new_workspace(64 << 20, DEV)
     for idx in (3, 1, 2, 3, 1, 2):
         w = W.build(idx, DEV)
@@ -215,5 +215,3 @@ def test_workspace_reuse_across_calls(gpu_lib):
         d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
         _say(f"[case] workspace reuse {w.spec.name}: {d_out:.3e} {d_lse:.3e}")
         assert d_out <= BF16_TOL and d_lse <= LSE_TOL
-    head = ws[:256].cpu()
-    assert int(head.sum()) == 0, "claim counters were not reset"
