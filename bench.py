@@ -64,16 +64,76 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, path: str):
+def measured_traffic(workload: str, path: str, schedule: str, part_size: int, depth: int):
     """HBM bytes per launch of the partition kernel from committed rocprofv3 counter runs, or None when
-    the kernels changed since they were taken."""
-    f = os.path.join(PROFILES, f"traffic_{path}_{workload}.json")
+    the kernels or the launch configuration changed since they were taken."""
+    f = os.path.join(PROFILES, f"traffic_{path}_{schedule}_{workload}.json")
     if not os.path.exists(f):
         return None
     d = json.load(open(f))
     if d.get("source_hash") != kernel_source_hash():
         return None
+    if d.get("partition_size") != part_size or d.get("pipeline_depth") != depth:
+        return None
     return d.get("bytes_per_launch")
+
+
+def decode_order_pages(w, part_size: int, rows_per_tile: int, waves: int):
+    """Per-wave K/V page lists in the order the persistent decode schedule visits them: items
+    (kv head, sequence, row tile, partition) kv-head-major, XCD x takes the x-th eighth of the items,
+    the waves of XCD x (workgroup i runs on XCD i % 8) take equal contiguous shares of it."""
+    KVH, B = w.spec.num_kv_heads, w.spec.block_size
+    G = w.spec.num_heads // KVH
+    PP = part_size // B
+    items = []
+    for kvh in range(KVH):
+        for s in range(w.num_seqs):
+            n = int(w.context_lens[s])
+            nblk = (n + B - 1) // B
+            row_ids = w.block_tables[s, :nblk].astype(np.int64) * KVH + kvh
+            rts = -(-int(w.q_lens[s]) * G // rows_per_tile)
+            for _ in range(rts):
+                for p in range(-(-nblk // PP)):
+                    items.append(row_ids[p * PP:(p + 1) * PP])
+    L = len(items)
+    wgs = waves // 4
+    lists = [np.zeros(0, np.int64)] * waves
+    for x in range(8):
+        lo, hi = L * x // 8, L * (x + 1) // 8
+        n_wg = (wgs - x + 7) // 8
+        W = n_wg * 4
+        for wx in range(W):
+            a, b = lo + (hi - lo) * wx // W, lo + (hi - lo) * (wx + 1) // W
+            if b > a:
+                lists[((wx // 4) * 8 + x) * 4 + wx % 4] = np.concatenate(items[a:b])
+    return lists
+
+
+def pattern_ceiling(w, plan, k_cache, v_cache, reps: int = 3):
+    """Time the page-stream probe (same loads as the decode kernel, no arithmetic) on this workload's
+    pages in the decode schedule's order.  Returns (seconds, pages streamed)."""
+    import torch
+
+    from paged_kv_cache_199_amd import _lib
+
+    lists = decode_order_pages(w, plan["partition_size"], plan["rows_per_tile"], plan["grid_waves"])
+    offs = np.zeros(len(lists) + 1, np.int64)
+    offs[1:] = np.cumsum([len(l) for l in lists])
+    dev = k_cache.device
+    flat = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(dev)
+    off_t = torch.from_numpy(offs.astype(np.int32)).to(dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    _lib.probe_page_stream(k_cache, v_cache, flat, off_t, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        _lib.probe_page_stream(k_cache, v_cache, flat, off_t, sink)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    return float(np.median(times)), int(offs[-1])
 
 
 def cpu_baseline(w, budget_s: float):
@@ -128,6 +188,7 @@ def main():
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -215,7 +276,8 @@ def main():
     tokens = int(w.context_lens.astype(np.int64).sum())
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(spec.name, kernel.split("_")[1])
+    sched_name = ["", "grid", "persistent"][plan["schedule"]]
+    traffic = measured_traffic(spec.name, kernel.split("_")[1], sched_name, P_used, plan["pipeline_depth"])
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + attended tokens/s, 1 GPU",
         "value": round(value, 2),
@@ -233,7 +295,7 @@ def main():
             "workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
             "head_dim": D, "block_size": spec.block_size, "q_len": w.max_q_len,
             "context_tokens": tokens, "max_context_len": w.max_context_len, "partition_size": P_used,
-            "path": kernel.split("_")[1], "schedule": ["", "grid", "persistent"][plan["schedule"]],
+            "path": kernel.split("_")[1], "schedule": sched_name,
             "pipeline_depth": plan["pipeline_depth"], "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -252,6 +314,16 @@ def main():
             "algorithmic_bytes_per_launch": dec_bytes,
         },
     }
+    if plan["schedule"] == 2 and not args.no_ceiling:
+        t_probe, pages = pattern_ceiling(w, plan, kcs[-1], vcs[-1])
+        ceil = dec_bytes / t_probe / 1e9
+        res["roofline"]["pattern_ceiling"] = {
+            "value": round(ceil, 2), "unit": "GB/s",
+            "what": "this workload's algorithmic bytes over the time the page-stream probe takes to read "
+                    f"the same {pages} K+V pages in the decode schedule's order with the decode loads "
+                    "and no arithmetic",
+        }
+        res["roofline"]["frac_of_pattern_ceiling"] = round(achieved / ceil, 4)
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(res), flush=True)

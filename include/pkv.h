@@ -119,6 +119,7 @@ typedef struct pkv_decode_plan_info {
   int row_tiles;           /* workgroups per (sequence, kv head, partition) */
   int pipeline_depth;      /* MFMA kernel register ring depth */
   int schedule;            /* PKV_SCHEDULE_GRID or PKV_SCHEDULE_PERSISTENT */
+  int grid_waves;          /* persistent schedule: waves of its grid on the current device; else 0 */
   size_t workspace_bytes;  /* same value as pkv_decode_workspace_bytes() */
 } pkv_decode_plan_info;
 

@@ -31,7 +31,7 @@ class DecodeOptions(ctypes.Structure):
 class DecodePlanInfo(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("num_partitions", _c_int), ("path", _c_int),
                 ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("pipeline_depth", _c_int),
-                ("schedule", _c_int), ("workspace_bytes", _c_sz)]
+                ("schedule", _c_int), ("grid_waves", _c_int), ("workspace_bytes", _c_sz)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -44,6 +44,7 @@ EXPORTS = {
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                        _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                        ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
+    "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_version": (_c_int, []),
 }
@@ -143,6 +144,18 @@ def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv
                                     head_dim, dtype_code, ctypes.byref(o), ctypes.byref(info)))
     _check(rc, "pkv_decode_plan")
     return {k: getattr(info, k) for k, _ in DecodePlanInfo._fields_}
+
+
+def probe_page_stream(k_cache: torch.Tensor, v_cache: torch.Tensor, page_index: torch.Tensor,
+                      wave_offsets: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper (include/pkv_probe.h): stream the listed K/V pages with the decode kernel's
+    load shapes and no arithmetic.  page_index / wave_offsets: int32 on the GPU."""
+    lib = load()
+    nb, kvh, B, D = k_cache.shape
+    _need(page_index.dtype == torch.int32 and wave_offsets.dtype == torch.int32, "int32 lists")
+    rc = lib.pkv_probe_page_stream(_ptr(k_cache), _ptr(v_cache), nb * kvh, D, _ptr(page_index),
+                                   _ptr(wave_offsets), wave_offsets.numel() - 1, _ptr(sink), _stream(stream))
+    _check(rc, "pkv_probe_page_stream")
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -85,9 +85,10 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
 
 // Policy.  Kernel: the matrix-core kernel for bf16, the vector-ALU kernel for fp32 (or when asked).
 // Rows per tile: the whole GQA group times the new tokens when it fits the kernel, else tiles.
-// Partition size: the largest of 512/256/128/64 keys that still gives
-// about 2048 live workgroups (8 per CU) for a mean context of half the maximum, and no split at all
-// when the whole context fits one partition.
+// Schedule: persistent for the matrix-core kernel when its limits allow, else the grid.  Partition
+// size: 512 keys for the persistent schedule; for the grid schedules the largest of 512/256/128/64
+// keys that still gives about 2048 live workgroups (8 per CU) for a mean context of half the
+// maximum.  No split at all when the whole context fits one partition.
 Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
                int num_kv_heads, int head_dim, int dtype, bool ragged_q,
                const pkv_decode_options *opts) {
@@ -114,7 +115,11 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
                                             : pkv::mfma_default_depth(head_dim, R, persist);
   if (persist && pl.depth == 3) pl.depth = 4;   // the persistent ring depth must divide 4
   int P = opts ? opts->partition_size : 0;
-  if (P == 0) {
+  if (P == 0 && persist) {
+    // a wave streams whole runs of partitions, so small partitions only add partials to merge;
+    // 512 keys measured best for 32x8 short, 256x8 long and 32x8x5-row verify batches
+    P = 512;
+  } else if (P == 0) {
     const int64_t units1 = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
     const int64_t mean_ctx = (max_context_len + 1) / 2;
     P = 64;
@@ -210,6 +215,10 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   info->rows_per_tile = pl.rows_per_tile;
   info->row_tiles = pl.row_tiles;
   info->pipeline_depth = pl.depth;
+  info->grid_waves = pl.schedule == PKV_SCHEDULE_PERSISTENT
+                         ? cu_count() * pkv::mfma_persistent_wgs_per_cu(head_dim, pl.rows_per_tile, pl.depth,
+                                                                         num_seqs) * 4
+                         : 0;
   info->schedule = pl.schedule;
   info->workspace_bytes = pl.bytes;
   return PKV_OK;

@@ -1,0 +1,91 @@
+// Page-stream probe (include/pkv_probe.h): the matrix-core decode kernel's K/V page loads with the
+// attention arithmetic taken out, to measure what the memory system delivers for a page pattern.
+#include "pkv.h"
+#include "pkv_probe.h"
+
+#include "device_common.h"
+
+namespace pkv {
+
+typedef const __attribute__((address_space(4))) int32_t const_i32_probe;
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict__ K, const char *__restrict__ V,
+                                                          int64_t pool_pages, const int32_t *__restrict__ list,
+                                                          const int32_t *__restrict__ offs, int num_waves,
+                                                          uint32_t *sink) {
+  constexpr int ROWB = D * 2;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= num_waves) return;
+  const int b0 = offs[w];
+  const int n = offs[w + 1] - b0;
+  if (n <= 0) return;
+  const const_i32_probe *ids = (const const_i32_probe *)(list + b0);   // read through the scalar cache
+  const int last = n - 1;
+  const int64_t page_bytes = (int64_t)kBlock * ROWB;
+  auto id_of = [&](int j) -> int64_t {
+    const int64_t id = ids[__builtin_amdgcn_readfirstlane(min(j, last))];
+    return id >= 0 && id < pool_pages ? id : 0;
+  };
+  uint32_t acc = 0;
+  uint4 kb[NBUF][NK];
+  uint2 vb[NBUF][ND];
+  auto issue = [&](int64_t id, uint4 *kr, uint2 *vr) {
+    const char *kp = K + id * page_bytes + col * ROWB + grp * 16;
+    #pragma unroll
+    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
+    const char *vp = V + id * page_bytes + (col * kBlock + 4 * grp) * 2;
+    #pragma unroll
+    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
+  };
+  auto use = [&](const uint4 *kr, const uint2 *vr) {
+    #pragma unroll
+    for (int c = 0; c < NK; ++c) acc += kr[c].x ^ kr[c].w;
+    #pragma unroll
+    for (int t = 0; t < ND; ++t) acc += vr[t].x ^ vr[t].y;
+  };
+  int64_t sid[NBUF];
+  #pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) issue(id_of(j), kb[j], vb[j]);
+  #pragma unroll
+  for (int b = 0; b < NBUF; ++b) sid[b] = id_of(NBUF - 1 + b);
+  int j0 = 0;
+  for (; j0 + NBUF <= n; j0 += NBUF) {
+    #pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int bn = (b + NBUF - 1) % NBUF;
+      issue(sid[b], kb[bn], vb[bn]);
+      sid[b] = id_of(j0 + b + 2 * NBUF - 1);
+      use(kb[b], vb[b]);
+    }
+  }
+  #pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b)
+    if (j0 + b < n) use(kb[b], vb[b]);
+  if (acc == 0x5a5a5a5au) sink[0] = acc;   // practically never true; keeps the loads
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_probe_page_stream(const void *k_pool, const void *v_pool, int64_t pool_pages, int head_dim,
+                                     const int32_t *page_index, const int32_t *wave_offsets, int num_waves,
+                                     uint32_t *sink, void *stream) {
+  if (!k_pool || !v_pool || !page_index || !wave_offsets || !sink) return PKV_ERR_NULL;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (num_waves < 0 || pool_pages < 1) return PKV_ERR_SHAPE;
+  if (num_waves == 0) return PKV_OK;
+  const int grid = (num_waves + 3) / 4;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char *K = static_cast<const char *>(k_pool);
+  const char *V = static_cast<const char *>(v_pool);
+  if (head_dim == 64)
+    pkv::page_stream_kernel<64, 3><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+  else
+    pkv::page_stream_kernel<128, 3><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
