@@ -14,6 +14,7 @@ the launch stream.  `cpu_baseline` times the float64 oracle on the host on a bou
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -26,6 +27,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -78,62 +80,74 @@ def measured_traffic(workload: str, path: str, schedule: str, part_size: int, de
     return d.get("bytes_per_launch")
 
 
-def decode_order_pages(w, part_size: int, rows_per_tile: int, waves: int):
-    """Per-wave K/V page lists in the order the persistent decode schedule visits them: items
-    (kv head, sequence, row tile, partition) kv-head-major, XCD x takes the x-th eighth of the items,
-    the waves of XCD x (workgroup i runs on XCD i % 8) take equal contiguous shares of it."""
+def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int):
+    """Per-wave K/V page lists in the order the persistent decode schedule visits them: the stream of
+    pages (kv head, sequence, row tile, logical page) kv-head-major, cut into NW equal shares (share
+    x * W + wx goes to wave wx of XCD x; workgroup i runs on XCD i % 8), each boundary that falls
+    inside a work item moved down to a multiple of cut_align pages from the item's start."""
     KVH, B = w.spec.num_kv_heads, w.spec.block_size
     G = w.spec.num_heads // KVH
-    PP = part_size // B
-    items = []
+    parts, starts = [], []
+    pos = 0
     for kvh in range(KVH):
         for s in range(w.num_seqs):
-            n = int(w.context_lens[s])
-            nblk = (n + B - 1) // B
+            nblk = (int(w.context_lens[s]) + B - 1) // B
             row_ids = w.block_tables[s, :nblk].astype(np.int64) * KVH + kvh
             rts = -(-int(w.q_lens[s]) * G // rows_per_tile)
             for _ in range(rts):
-                for p in range(-(-nblk // PP)):
-                    items.append(row_ids[p * PP:(p + 1) * PP])
-    L = len(items)
-    wgs = waves // 4
+                parts.append(row_ids)
+                starts.append(pos)
+                pos += nblk
+    stream = np.concatenate(parts)
+    starts = np.asarray(starts, np.int64)
+    L = len(stream)
+    W = waves // 8
+
+    def raw(o):
+        return L * o // (8 * W)
+
+    def cut(b):
+        if b >= L:
+            return L
+        st = starts[np.searchsorted(starts, b, side="right") - 1]
+        return b - (b - st) % cut_align
+
     lists = [np.zeros(0, np.int64)] * waves
-    for x in range(8):
-        lo, hi = L * x // 8, L * (x + 1) // 8
-        n_wg = (wgs - x + 7) // 8
-        W = n_wg * 4
-        for wx in range(W):
-            a, b = lo + (hi - lo) * wx // W, lo + (hi - lo) * (wx + 1) // W
-            if b > a:
-                lists[((wx // 4) * 8 + x) * 4 + wx % 4] = np.concatenate(items[a:b])
+    for o in range(8 * W):
+        a, b = cut(raw(o)), cut(raw(o + 1))
+        x, wx = divmod(o, W)
+        lists[((wx // 4) * 8 + x) * 4 + wx % 4] = stream[a:b]
     return lists
 
 
-def pattern_ceiling(w, plan, k_cache, v_cache, reps: int = 3):
+def pattern_ceiling(w, plan, kcs, vcs, reps: int = 3):
     """Time the page-stream probe (same loads as the decode kernel, no arithmetic) on this workload's
-    pages in the decode schedule's order.  Returns (seconds, pages streamed)."""
+    pages in the decode schedule's order, rotating over the same pool copies as the timed steps.
+    Returns (seconds per launch, pages streamed)."""
     import torch
 
     from paged_kv_cache_199_amd import _lib
 
-    lists = decode_order_pages(w, plan["partition_size"], plan["rows_per_tile"], plan["grid_waves"])
+    cut_align = plan["pipeline_depth"] if plan["num_partitions"] > 1 else 1
+    lists = decode_order_pages(w, plan["rows_per_tile"], plan["grid_waves"], cut_align)
     offs = np.zeros(len(lists) + 1, np.int64)
     offs[1:] = np.cumsum([len(l) for l in lists])
-    dev = k_cache.device
+    dev = kcs[0].device
     flat = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(dev)
     off_t = torch.from_numpy(offs.astype(np.int32)).to(dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    _lib.probe_page_stream(k_cache, v_cache, flat, off_t, sink)
+    R = len(kcs)
+    for r in range(R):
+        _lib.probe_page_stream(kcs[r], vcs[r], flat, off_t, sink)
     torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        _lib.probe_page_stream(k_cache, v_cache, flat, off_t, sink)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e-3)
-    return float(np.median(times)), int(offs[-1])
+    n = reps * R
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        _lib.probe_page_stream(kcs[i % R], vcs[i % R], flat, off_t, sink)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / n, int(offs[-1])
 
 
 def cpu_baseline(w, budget_s: float):
@@ -189,6 +203,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
+    ap.add_argument("--no-graph", action="store_true", help="time the eager step only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -242,20 +257,36 @@ def main():
     q_lens = None if w.uniform_q else meta["q_lens"]
     stream = torch.cuda.current_stream()
     total = args.warmup + args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for b, e in ev:           # create the underlying hipEvents so their handles can be passed down
-        b.record(stream)
-        e.record(stream)
+    # Timing events around the partition kernel, recorded by the library on its stream.  They skip
+    # the system-scope cache writeback / invalidate a default event performs when it is recorded,
+    # which would otherwise add several microseconds of idle GPU next to the kernel being timed.
+    hip = ctypes.CDLL("libamdhip64.so.7")     # the HIP runtime torch already loaded
+
+    def new_event():
+        e = ctypes.c_void_p()
+        if hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def elapsed_ms(a, b):
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    ev = [(new_event(), new_event()) for _ in range(args.steps)]
+
+    dstep = _lib.DecodeStep(w.q, kcs[0], vcs[0], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
+                            H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
+                            partition_size=P, path=path, depth=args.depth, schedule=sched, workspace=ws,
+                            new_k=w.new_k, new_v=w.new_v,
+                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None else None)
 
     def step(i, events=None):
         r = i % R
-        if w.slot_mapping is not None:
-            _lib.kv_cache_write(w.new_k, w.new_v, meta["slot_mapping"], kcs[r], vcs[r])
-        _lib.paged_attn_decode(w.q, kcs[r], vcs[r], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
-                               H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
-                               partition_size=P, path=path, workspace=ws, events=events, depth=args.depth,
-                               schedule=sched)
+        dstep(kcs[r], vcs[r], events=events)
 
+    # eager: every step is two C calls from Python; HIP events around the partition kernel
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -266,10 +297,45 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i, ev[i])
     t_end.record(stream)
+    host_enqueue = time.perf_counter() - wall0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    k_ms = float(np.mean([b.elapsed_time(e) for b, e in ev]))
+    eager_ms_step = t_start.elapsed_time(t_end) / args.steps
+    k_ms = float(np.mean([elapsed_ms(b, e) for b, e in ev]))
+    for b, e in ev:
+        hip.hipEventDestroy(b)
+        hip.hipEventDestroy(e)
+    ms_step = eager_ms_step
+    timing = "eager"
+    graph_ok = None
+    if not args.no_graph:
+        # the same K steps captured into one HIP graph and replayed: no host work between steps
+        ref_out = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        wallg = time.perf_counter()
+        g0.record(stream)
+        graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - wallg
+        ms_step = g0.elapsed_time(g1) / args.steps
+        timing = "hip graph replay of the K steps"
+        graph_ok = bool(torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                                    ref_out.view(torch.int16) if out.dtype == torch.bfloat16 else ref_out))
+        del graph
 
     dec_bytes = algorithmic_bytes(w)
     step_bytes = dec_bytes + write_bytes(w)
@@ -301,6 +367,10 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
+        "step_timing": timing,
+        "eager_ms_per_step": round(eager_ms_step, 5),
+        "eager_host_us_per_step": round(host_enqueue / args.steps * 1e6, 2),
+        "graph_matches_eager": graph_ok,
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",
@@ -315,7 +385,7 @@ def main():
         },
     }
     if plan["schedule"] == 2 and not args.no_ceiling:
-        t_probe, pages = pattern_ceiling(w, plan, kcs[-1], vcs[-1])
+        t_probe, pages = pattern_ceiling(w, plan, kcs, vcs)
         ceil = dec_bytes / t_probe / 1e9
         res["roofline"]["pattern_ceiling"] = {
             "value": round(ceil, 2), "unit": "GB/s",

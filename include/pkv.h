@@ -66,8 +66,10 @@ typedef enum pkv_path { PKV_PATH_AUTO = 0, PKV_PATH_VALU = 1, PKV_PATH_MFMA = 2 
 
 /* How partition work maps onto the GPU (matrix-core kernel).  GRID: one workgroup per (kv head,
  * partition, sequence, row tile) of a grid sized from the host maxima.  PERSISTENT: a few workgroups
- * per CU whose waves walk the live partitions listed from context_lens (num_seqs <= 4096, partitions
- * of a multiple of 64 and at most 1024 keys; ring depth 2 or 4).  AUTO lets the library choose. */
+ * per CU; every wave takes an equal share (to within the ring depth) of the K/V pages all work items
+ * read, listed from context_lens, so a long sequence is split wherever a share ends and its pieces
+ * are merged like partitions (num_seqs <= 4096, ring depth 2 or 4; partitions are optional here).
+ * AUTO lets the library choose. */
 typedef enum pkv_schedule {
   PKV_SCHEDULE_AUTO = 0, PKV_SCHEDULE_GRID = 1, PKV_SCHEDULE_PERSISTENT = 2
 } pkv_schedule;
@@ -75,9 +77,10 @@ typedef enum pkv_schedule {
 /* Optional tuning / instrumentation for pkv_paged_attn_decode.  Pass NULL for defaults; a zeroed
  * struct also means defaults. */
 typedef struct pkv_decode_options {
-  int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy;
-                               values above 4096 are clamped; the persistent schedule rounds up to
-                               a multiple of 64 and clamps to 1024 */
+  int partition_size;       /* keys per split-K partition, a multiple of block_size; 0 = policy
+                               (the persistent schedule then uses none); the grid schedules clamp
+                               values above 4096; the persistent schedule rounds up to a multiple of
+                               64 */
   int path;                 /* pkv_path */
   int pipeline_depth;       /* MFMA kernel: pages of K/V held per wave (2..4); 0 = policy */
   int schedule;             /* pkv_schedule */
@@ -103,8 +106,10 @@ int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping
 
 /*
  * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options (0 is possible:
- * a single-partition launch with uniform q needs none).  The split-K partials take
- * ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes.
+ * a single-partition grid launch with uniform q needs none).  The split-K partials take
+ * ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes; the persistent
+ * schedule adds (num_seqs + 1) * 4 bytes and rows_per_tile * (head_dim + 1) * 4 bytes per wave of
+ * its grid (the value depends on the device's CU count).
  */
 size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int max_context_len,
                                   int num_heads, int num_kv_heads, int head_dim, int dtype,
@@ -130,7 +135,8 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
 
 /*
  * Paged decode attention (definition at the top of this file), with a split-K pass over key
- * partitions of P tokens merged through their log-sum-exp (lfm25-inference, "Runtime Design").
+ * partitions merged through their log-sum-exp (lfm25-inference, "Runtime Design"): partitions of P
+ * tokens, and under the persistent schedule also the pieces its page-balanced split cuts.
  * Preconditions on device data: 1 <= q_lens[s] <= context_lens[s] <= max_context_len,
  * context_lens[s] <= max_blocks_per_seq * block_size, block ids in [0, num_blocks), and
  * sum(q_lens) == total_q (q_lens == NULL: total_q == num_seqs * max_q_len).

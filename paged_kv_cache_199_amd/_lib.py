@@ -203,3 +203,85 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                                    num_heads, num_kv_heads, head_dim, block_size, float(scale), code,
                                    ctypes.byref(o), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_paged_attn_decode")
+
+
+class DecodeStep:
+    """One decode step bound once: the optional slot-mapped append of the new tokens' K/V, then paged
+    decode attention, with the same checks as kv_cache_write / paged_attn_decode done at
+    construction.  A call only enqueues the two C calls on the current stream, so a serving loop
+    pays little host time per step and the step can be captured in a HIP graph.  A call may swap in
+    other cache tensors of the same shape, dtype and device (not checked again)."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
+                 num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len=1,
+                 partition_size=0, path=PATH_AUTO, depth=0, schedule=0, workspace=None,
+                 new_k=None, new_v=None, slot_mapping=None):
+        lib = load()
+        self._lib = lib
+        total_q = q.shape[0]
+        S = context_lens.numel()
+        NB = k_cache.shape[0]
+        # the full checks of the one-shot calls, once
+        _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
+        _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
+        _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
+        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+        for t in (q, k_cache, v_cache, out):
+            _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "same dtype, contiguous, on the GPU")
+        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
+              and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
+        _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
+        if q_lens is not None:
+            _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(),
+                  "q_lens: int32 [S]")
+        if lse is not None:
+            _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads)
+                  and lse.is_contiguous(), "lse: fp32 [total_q, H]")
+        code = _dtype_code(q)
+        self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None)
+        self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None)
+        need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
+                                                  num_kv_heads, head_dim, code, ctypes.byref(self._opts)))
+        if workspace is None and need > 0:
+            workspace = new_workspace(need, q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _need(ws_bytes >= need, "workspace too small")
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, workspace,
+                      new_k, new_v, slot_mapping)
+        self._head = (_ptr(q),)
+        self._mid = (_ptr(block_tables), _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),
+                     S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB,
+                     num_heads, num_kv_heads, head_dim, block_size, float(scale), code)
+        self._tail = (_ptr(workspace), ws_bytes)
+        self._write = None
+        if slot_mapping is not None:
+            T = new_k.shape[0]
+            _need(new_k.dim() == 3 and new_k.shape == new_v.shape and tuple(new_k.shape[1:]) == (num_kv_heads, head_dim),
+                  "new_k / new_v must be [T, KVH, D]")
+            _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T and slot_mapping.is_contiguous()
+                  and slot_mapping.is_cuda, "slot_mapping: int64 [T] on the GPU")
+            for t in (new_k, new_v):
+                _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, on the GPU")
+            self._write = ((_ptr(new_k), _ptr(new_v), _ptr(slot_mapping)),
+                           (T, NB, num_kv_heads, head_dim, block_size, code))
+        self._kc, self._vc = _ptr(k_cache), _ptr(v_cache)
+
+    def __call__(self, k_cache=None, v_cache=None, events=None, stream=None):
+        kc = self._kc if k_cache is None else ctypes.c_void_p(k_cache.data_ptr())
+        vc = self._vc if v_cache is None else ctypes.c_void_p(v_cache.data_ptr())
+        st = _stream(stream)
+        lib = self._lib
+        if self._write is not None:
+            ptrs, sizes = self._write
+            rc = lib.pkv_kv_cache_write(*ptrs, kc, vc, *sizes, st)
+            if rc != 0:
+                _check(rc, "pkv_kv_cache_write")
+        o = self._opts
+        if events is not None:
+            # torch.cuda.Event objects, or raw hipEvent_t handles
+            o = self._opts_ev
+            o.event_main_begin = getattr(events[0], "cuda_event", events[0])
+            o.event_main_end = getattr(events[1], "cuda_event", events[1])
+        rc = lib.pkv_paged_attn_decode(*self._head, kc, vc, *self._mid, ctypes.byref(o), *self._tail, st)
+        if rc != 0:
+            _check(rc, "pkv_paged_attn_decode")

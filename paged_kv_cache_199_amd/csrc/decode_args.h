@@ -33,6 +33,12 @@ struct DecodeArgs {
   int row_tiles;               // row tiles per (sequence, kv head)
   int units;                   // num_kv_heads * num_parts * num_seqs * row_tiles
   int per_xcd;                 // ceil(units / 8)
+  // balanced (persistent) schedule only
+  int32_t *item_pre;           // [num_seqs + 1] stream pages of one kv head before each sequence
+  int64_t spill_base;          // first spill row of part_o / part_lse; -1: no spill rows (grid)
+  int share_waves;             // waves per XCD in the persistent grid
+  int cut_align;               // share boundaries inside a work item fall on multiples of this
+  int rows_per_tile;
 };
 
 // Per-unit sequence facts with the clamps that keep bad metadata memory-safe.
@@ -54,6 +60,34 @@ __device__ __forceinline__ SeqInfo load_seq(const DecodeArgs &a, int s) {
   si.qbase = a.q_start ? a.q_start[s] : s * a.max_q_len;
   si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
   return si;
+}
+
+// The balanced schedule's page stream: for each kv head, for each sequence, for each row tile, the
+// sequence's pages in logical order; kv head kvh's part starts at kvh * I (I = pages per kv head, so
+// L = I * num_kv_heads in all).  Share `ord` of the NW = 8 W waves starts at floor(L ord / NW);
+// ord = x * W + wx is wave wx of XCD x, so each XCD takes one contiguous eighth of the stream.  A
+// boundary that falls inside a work item moves down to a multiple of cut_align pages from the
+// item's start (1 when no partitions are asked for), so a share starts where its ring cycles can.
+// L ord < 2^53, so the double quotient has the exact floor: it is correctly rounded, and an integer
+// quotient is representable.
+__device__ __forceinline__ int64_t share_raw(int64_t L, int NW, int ord) {
+  return (int64_t)floor((double)L * (double)ord / (double)NW);
+}
+
+// Smallest share whose raw start lies above pos, for 0 <= pos < L: the double estimate of
+// ceil((pos + 1) NW / L) is at most one below it; step up with exact comparisons.
+__device__ __forceinline__ int first_share_above(int64_t L, int NW, int64_t pos) {
+  int c = (int)floor((double)(pos + 1) * (double)NW / (double)L) - 1;
+  c = max(c, 0);
+  while (c < NW && share_raw(L, NW, c) <= pos) ++c;
+  return c;
+}
+
+// Workgroup-wave slot of share ord: workgroup (wx / 4) * 8 + x, wave wx % 4.
+__device__ __forceinline__ int share_slot(int W, int ord) {
+  const int x = ord / W;
+  const int wx = ord - x * W;
+  return (((wx >> 2) << 3) + x) * 4 + (wx & 3);
 }
 
 }  // namespace pkv

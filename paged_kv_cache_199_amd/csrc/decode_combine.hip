@@ -10,10 +10,12 @@
 
 namespace pkv {
 
-// One wave per (sequence, new token, head); partition LSEs are in log2 units.  The LSEs of up to 64
-// partitions are read at once (one per lane), their max and weight sum are wave reductions, and the
-// weights are broadcast from the lane that holds them, so the partial outputs stream with several
-// loads in flight instead of one dependent load per partition.
+// One wave per (sequence, new token, head); partial LSEs are in log2 units.  The sources of a row are
+// its partitions and, under the balanced schedule, the spill rows of the shares that start inside
+// the row's work item.  The LSEs of up to 64 sources are read at once (one per lane), their max and
+// weight sum are wave reductions, and the weights and row offsets are broadcast from the lane that
+// holds them, so the partial outputs stream with several loads in flight instead of one dependent
+// load per source.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int DPL = D / 64;
@@ -26,51 +28,121 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int64_t t = wid / H;
   const int i = (int)(t % a.max_q_len);
   const int s = (int)(t / a.max_q_len);
+  // issued before the sequence's lengths come back: they do not depend on them
+  const bool spill = a.spill_base >= 0;
+  const int pre_s = spill ? a.item_pre[s] : 0;
+  const int pre_all = spill ? a.item_pre[a.num_seqs] : 0;
   const SeqInfo si = load_seq(a, s);
-  if (si.nparts <= 1 || i >= si.qs) return;
+  if (i >= si.qs || si.ctx <= 0) return;
   const int row = si.qbase + i;
   if (row >= a.total_q) return;
   const int64_t stride = (int64_t)a.total_q * H;          // between partitions
   const int64_t base = (int64_t)row * H + h;
 
+  // shares that start inside this row's work item [pos0, pos1) of the balanced stream
+  int ncand = 0, ord0 = 0, srow = 0;
+  int64_t pos0 = 0, pos1 = 0, L = 0;
+  const int W = a.share_waves;
+  const int NW = 8 * W;
+  const int N = a.cut_align;                              // 1, 2 or 4
+  const int PP = a.part_size / kBlock;
+  if (spill) {
+    const int G = a.group;
+    const int rloc = i * G + h % G;
+    const int rt = rloc / a.rows_per_tile;
+    srow = rloc - rt * a.rows_per_tile;
+    const int nblk = (si.ctx + kBlock - 1) / kBlock;
+    const int I = pre_all;
+    L = (int64_t)I * a.num_kv_heads;
+    pos0 = (int64_t)(h / G) * I + pre_s + (int64_t)rt * nblk;
+    pos1 = pos0 + nblk;
+    ord0 = first_share_above(L, NW, pos0);
+    ncand = max(0, first_share_above(L, NW, pos1 - 1) - ord0);
+  }
+  // source idx < nparts: partition idx; else candidate share ord0 + idx - nparts, a source when its
+  // rounded start is inside the item, not on a partition start, and its share is not empty
+  auto source = [&](int idx, int64_t &prow, bool &cut) -> bool {
+    cut = false;
+    if (idx < si.nparts) {
+      prow = idx * stride + base;
+      return true;
+    }
+    const int ord = ord0 + idx - si.nparts;
+    const int64_t b = share_raw(L, NW, ord);                // in (pos0, pos1)
+    const int ob = (int)(b - pos0) & ~(N - 1);              // rounded offset in the item
+    if (ob <= 0) return false;
+    cut = true;
+    if (ob % PP == 0) return false;
+    const int64_t bn = share_raw(L, NW, ord + 1);
+    const int64_t obn = bn < pos1 ? (int)(bn - pos0) & ~(N - 1) : bn - pos0;
+    if (obn <= ob) return false;
+    prow = a.spill_base + (int64_t)share_slot(W, ord) * a.rows_per_tile + srow;
+    return true;
+  };
+  const int nsrc = si.nparts + ncand;
+
+  // the first 64 sources (usually all of them) are resolved once and kept for the second pass
+  float M = -INFINITY;
+  bool any_cut = false;
+  int64_t prow0 = base;   // a non-source lane points at partition 0's row (always written), weight 0
+  float lse0 = -INFINITY;
+  for (int c0 = 0; c0 < nsrc; c0 += 64) {
+    int64_t prow = base;
+    bool cut = false;
+    const bool ok = c0 + lane < nsrc && source(c0 + lane, prow, cut);
+    any_cut |= cut;
+    const float l = ok ? a.part_lse[prow] : -INFINITY;
+    if (c0 == 0) {
+      prow0 = prow;
+      lse0 = l;
+    }
+    M = fmaxf(M, l);
+  }
+  // a row whose item one wave covered in one piece already holds its final output
+  if (si.nparts <= 1 && __builtin_amdgcn_ballot_w64(any_cut) == 0) return;
+  M = wave_max(M);
+  const float Ms = M == -INFINITY ? 0.f : M;
+
   float acc[DPL];
   #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-  float M = -INFINITY;
-  for (int p = lane; p < si.nparts; p += 64) M = fmaxf(M, a.part_lse[p * stride + base]);
-  M = wave_max(M);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  for (int c0 = 0; c0 < si.nparts; c0 += 64) {
-    const int pl = c0 + lane;
-    const float wl = pl < si.nparts ? exp2_hw(a.part_lse[pl * stride + base] - Ms) : 0.f;
-    L += wl;
-    const int n = min(64, si.nparts - c0);
-    const float *op = a.part_o + (c0 * stride + base) * D + lane;
-    int j = 0;
-    for (; j + 8 <= n; j += 8) {
-      float v[8][DPL];
+  float L2 = 0.f;
+  for (int c0 = 0; c0 < nsrc; c0 += 64) {
+    int64_t prow = prow0;
+    float l = lse0;
+    if (c0 > 0) {
+      bool cut = false;
+      prow = base;
+      l = c0 + lane < nsrc && source(c0 + lane, prow, cut) ? a.part_lse[prow] : -INFINITY;
+    }
+    const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
+    L2 += wl;
+    const int lo = (int)prow;
+    const int hi = (int)(prow >> 32);
+    const int n = min(64, nsrc - c0);
+    // batches of 16 sources, all loads of a batch in flight together; a lane past the chunk's end
+    // reads partition 0's row with weight 0
+    for (int j = 0; j < n; j += 16) {
+      float v[16][DPL];
       #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
+        const int src = min(j + u, 63);
+        const int64_t pr = j + u < n ? ((int64_t)__shfl(hi, src) << 32) | (uint32_t)__shfl(lo, src) : base;
+        const float *op = a.part_o + pr * D + lane;
         #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = op[(j + u) * stride * D + 64 * k];
+        for (int k = 0; k < DPL; ++k) v[u][k] = op[64 * k];
       }
       #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wp = __shfl(wl, j + u);
+      for (int u = 0; u < 16; ++u) {
+        const float wp = j + u < n ? __shfl(wl, min(j + u, 63)) : 0.f;
         #pragma unroll
         for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, v[u][k], acc[k]);
       }
     }
-    for (; j < n; ++j) {
-      const float wp = __shfl(wl, j);
-      #pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, op[j * stride * D + 64 * k], acc[k]);
-    }
   }
-  L = wave_sum(L);
-  const bool seen = L > 0.f;
-  const float inv = seen ? 1.f / L : 0.f;
+  L2 = wave_sum(L2);
+  const bool seen = L2 > 0.f;
+  const float inv = seen ? 1.f / L2 : 0.f;
   #pragma unroll
   for (int k = 0; k < DPL; ++k) {
     const float o = acc[k] * inv;
@@ -80,7 +152,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       static_cast<float *>(a.out)[base * D + lane + 64 * k] = o;
     }
   }
-  if (lane == 0 && a.lse) a.lse[base] = seen ? (Ms + log2_hw(L)) * kLn2 : -INFINITY;
+  if (lane == 0 && a.lse) a.lse[base] = seen ? (Ms + log2_hw(L2)) * kLn2 : -INFINITY;
 }
 
 // Exclusive prefix sum of q_lens into q_start[0..n]; one workgroup of 1024 threads.

@@ -128,8 +128,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// LDS tables of the persistent schedule, per sequence s: pre = items of sequences < s (for one kv
-// head), ctx = clamped context length, qb = first q row, rts = row tiles, qs = clamped new tokens.
+// LDS tables of the persistent schedule, per sequence s: pre = stream pages of sequences < s (for
+// one kv head), ctx = clamped context length, qb = first q row, rts = row tiles, qs = clamped new
+// tokens.  Workgroup 0 also leaves pre in the workspace for the combine kernel.
 template <int D, int NT, int NBUF>
 __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs a) {
   constexpr int ROWS = 16 * NT;
@@ -148,81 +149,101 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
   const int G = a.group;
 
   if (wave == 0) {
-    int run_items = 0, run_q = 0;
+    const bool publish = blockIdx.x == 0;
+    int run_pages = 0, run_q = 0;
     for (int base = 0; base < S; base += 64) {
       const int s = base + lane;
-      int ctx = 0, qs = 0, qraw = 0, items = 0, rt = 1;
+      int ctx = 0, qs = 0, qraw = 0, pages = 0, rt = 1;
       if (s < S) {
         ctx = min(min(a.context_lens[s], a.max_context_len), a.max_blocks_per_seq * kBlock);
         ctx = max(ctx, 0);
         qraw = max(a.q_lens ? a.q_lens[s] : a.max_q_len, 0);
         qs = max(1, min(qraw, ctx));
         rt = (qs * G + ROWS - 1) / ROWS;
-        items = (ctx + a.part_size - 1) / a.part_size * rt;
+        pages = (ctx + kBlock - 1) / kBlock * rt;
       }
-      const int inc_items = wave_incl_scan(items, lane);
+      const int inc_pages = wave_incl_scan(pages, lane);
       const int inc_q = wave_incl_scan(qraw, lane);
       if (s < S) {
-        pre[s + 1] = run_items + inc_items;
+        pre[s + 1] = run_pages + inc_pages;
+        if (publish) a.item_pre[s + 1] = run_pages + inc_pages;
         tctx[s] = ctx;
         tqb[s] = run_q + inc_q - qraw;
         trts[s] = rt;
         tqs[s] = qs;
       }
-      run_items += __shfl(inc_items, 63);
+      run_pages += __shfl(inc_pages, 63);
       run_q += __shfl(inc_q, 63);
     }
-    if (lane == 0) pre[0] = 0;
+    if (lane == 0) {
+      pre[0] = 0;
+      if (publish) a.item_pre[0] = 0;
+    }
   }
   __syncthreads();
 
-  const int I = pre[S];                             // items per kv head
-  const int64_t L = (int64_t)I * a.num_kv_heads;    // all items
-  const int xcd = blockIdx.x & 7;
-  const int n_wg = (int)((gridDim.x - xcd + 7) >> 3);
-  const int64_t lo = L * xcd / 8;
-  const int64_t span = L * (xcd + 1) / 8 - lo;
-  const int W = n_wg * 4;
-  const int wx = (blockIdx.x >> 3) * 4 + wave;
-  const int64_t k_end = lo + span * (wx + 1) / W;
+  const int I = pre[S];                             // stream pages per kv head
+  const int64_t L = (int64_t)I * a.num_kv_heads;
+  const int W = a.share_waves;
+  const int NW = 8 * W;
+  const int N = a.cut_align;
+  const int ord = (blockIdx.x & 7) * W + (blockIdx.x >> 3) * 4 + wave;
+  const int64_t spill_row0 = a.spill_base + (int64_t)(blockIdx.x * 4 + wave) * ROWS;
   const int PP = a.part_size / kBlock;
-  int64_t k = lo + span * wx / W;
-  // Items are ordered (kv head, sequence, row tile, partition): the wave's contiguous share walks
-  // runs of consecutive partitions of one (sequence, kv head, row tile) as one page stream.
-  while (k < k_end) {
-    const int kvh = (int)(k / I);
-    const int r = (int)(k - (int64_t)kvh * I);
-    int s0 = 0, s1 = S;                              // pre[s0] <= r < pre[s1]
+
+  // sequence holding stream offset r of one kv head: the last s with pre[s] <= r (never an empty one)
+  auto seq_of = [&](int r) {
+    int s0 = 0, s1 = S;
     while (s1 - s0 > 1) {
       const int mid = (s0 + s1) >> 1;
       if (pre[mid] <= r) s0 = mid;
       else s1 = mid;
     }
+    return s0;
+  };
+  auto cut = [&](int64_t b) -> int64_t {
+    if (b >= L) return L;
+    const int kvh = (int)(b / I);
+    const int r = (int)(b - (int64_t)kvh * I);
+    const int s = seq_of(r);
+    const int nblk = (tctx[s] + kBlock - 1) / kBlock;
+    return b - ((r - pre[s]) % nblk) % N;
+  };
+  int64_t k = cut(share_raw(L, NW, ord));
+  const int64_t k_end = cut(share_raw(L, NW, ord + 1));
+  // The share walks its work items in stream order.  A piece that covers a whole item of a sequence
+  // with one partition is final; any other piece leaves a partial: the row of its partition when it
+  // starts a partition, else (only the share's first piece can start inside one) this wave's spill
+  // rows.
+  while (k < k_end) {
+    const int kvh = (int)(k / I);
+    const int r = (int)(k - (int64_t)kvh * I);
     // LDS reads come back in vector registers; the values are wave-uniform, and saying so keeps the
     // block-table row pointer scalar (its page ids then come through the scalar cache)
-    const int s = __builtin_amdgcn_readfirstlane(s0);
+    const int s = __builtin_amdgcn_readfirstlane(seq_of(r));
     SeqInfo si;
     si.ctx = __builtin_amdgcn_readfirstlane(tctx[s]);
     si.qs = __builtin_amdgcn_readfirstlane(tqs[s]);
     si.qbase = __builtin_amdgcn_readfirstlane(tqb[s]);
     si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
-    const int local = __builtin_amdgcn_readfirstlane(r - pre[s]);
-    const int rt = local / si.nparts;
-    const int p = local - rt * si.nparts;
-    const int m = (int)min((int64_t)(si.nparts - p), k_end - k);
     const int nblk = (si.ctx + kBlock - 1) / kBlock;
+    const int local = __builtin_amdgcn_readfirstlane(r - pre[s]);
+    const int rt = local / nblk;
+    const int j0 = local - rt * nblk;
+    const int run = (int)min((int64_t)(nblk - j0), k_end - k);
 
     WaveRows<D, NT> w;
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
     WaveAcc<D, NT> st;
     init_acc<D, NT>(st);
-    const bool single = si.nparts == 1;
-    stream_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq, p * PP,
-                              min((p + m) * PP, nblk), PP, lane, w, st, [&](int part) {
-                                finish_wave<D, NT>(a, part, single, lane, w, st);
+    stream_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq, j0, j0 + run,
+                              PP, lane, w, st, [&](int part, int first, int end) {
+                                const bool whole = first == 0 && end == nblk && si.nparts == 1;
+                                finish_wave<D, NT>(a, part, whole, lane, w, st,
+                                                   first % PP == 0 ? -1 : spill_row0);
                                 init_acc<D, NT>(st);
                               });
-    k += m;
+    k += run;
   }
 }
 

@@ -4,7 +4,8 @@
 //
 // One 64-thread workgroup per (new token, kv head).  K pages are token-major: the row is one
 // contiguous run, copied with 16-byte moves.  V pages are dim-major: element d of the row lands at
-// stride block_size, one element per lane.
+// stride block_size, one element per lane.  The source rows are read together with the slot (they
+// do not depend on it), so the kernel waits for memory once before it stores.
 #include "device_common.h"
 
 namespace pkv {
@@ -19,19 +20,26 @@ __global__ __launch_bounds__(64) void kv_write_kernel(const void *__restrict__ k
   const int64_t row = blockIdx.x;            // token * kvh_n + head
   const int64_t t = row / kvh_n;
   const int h = (int)(row - t * kvh_n);
+  static_assert(ROWB / 16 <= 64 && D % 64 == 0, "one 16-byte K chunk per lane, D / 64 V elements per lane");
+  constexpr int VPL = D / 64;
+  const int lane = threadIdx.x;
   const int64_t slot = slots[t];
+  const char *ks = static_cast<const char *>(k) + row * ROWB;
+  const bool kl = lane < ROWB / 16;
+  const uint4 kchunk = kl ? *reinterpret_cast<const uint4 *>(ks + lane * 16) : make_uint4(0, 0, 0, 0);
+  const elem_t *vs = static_cast<const elem_t *>(v) + row * D;
+  elem_t vv[VPL];
+  #pragma unroll
+  for (int e = 0; e < VPL; ++e) vv[e] = vs[lane + 64 * e];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / kBlock;
   const int off = (int)(slot - blk * kBlock);
-  const int lane = threadIdx.x;
   const int64_t page = blk * kvh_n + h;
-  const char *ks = static_cast<const char *>(k) + row * ROWB;
   char *kd = static_cast<char *>(kc) + (page * kBlock + off) * ROWB;
-  for (int c = lane; c < ROWB / 16; c += 64)
-    *reinterpret_cast<uint4 *>(kd + c * 16) = *reinterpret_cast<const uint4 *>(ks + c * 16);
-  const elem_t *vs = static_cast<const elem_t *>(v) + row * D;
+  if (kl) *reinterpret_cast<uint4 *>(kd + lane * 16) = kchunk;
   elem_t *vd = static_cast<elem_t *>(vc) + page * D * kBlock + off;
-  for (int d = lane; d < D; d += 64) vd[d * kBlock] = vs[d];
+  #pragma unroll
+  for (int e = 0; e < VPL; ++e) vd[(lane + 64 * e) * kBlock] = vv[e];
 }
 
 hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,

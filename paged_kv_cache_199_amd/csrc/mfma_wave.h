@@ -215,9 +215,10 @@ __device__ __forceinline__ void attend_pages(const DecodeArgs &a, const SeqInfo 
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // Attend the consecutive logical pages [jb, je) of one (sequence, kv head, row tile), flushing the
-// softmax state through flush(partition) after the last page of every partition of PP pages and
-// after page je - 1.  jb and PP are multiples of NBUF, so partition ends fall on the last page of a
-// ring cycle and the flush sits outside the unrolled cycle.  Page ids come through the scalar cache
+// softmax state through flush(partition, first page, end page) of each piece: after the last page of
+// every partition of PP pages and after page je - 1.  Either jb and PP are multiples of NBUF, or
+// the run lies inside one partition (PP >= je); so partition ends fall on the last page of a ring
+// cycle (or the run's end) and the flush sits outside the unrolled cycle.  Page ids come through the scalar cache
 // (the block table is read-only here): the id of the page issued NBUF steps later is fetched while
 // the current page is computed, so those loads never hold up the vector loads and a run of any
 // length streams without a restart.
@@ -262,6 +263,7 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   #pragma unroll
   for (int b = 0; b < NBUF; ++b) sid[b] = id_of(jb + NBUF - 1 + b);
   int j0 = 0;
+  int piece = jb;
   for (; j0 + NBUF <= n; j0 += NBUF) {
     #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
@@ -271,21 +273,26 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
       mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
     }
     const int jl = jb + j0 + NBUF - 1;
-    if ((jl + 1) % PP == 0 || jl == last) flush(jl / PP);
+    if ((jl + 1) % PP == 0 || jl == last) {
+      flush(jl / PP, piece, jl + 1);
+      piece = jl + 1;
+    }
   }
   if (j0 < n) {
     #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b)
       if (j0 + b < n) mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
-    flush(last / PP);
+    flush(last / PP, piece, je);
   }
 }
 
 // Finish one wave's rows without other waves: fold the exp-sum over the column's 4 lanes and write
-// either the final output (bf16) + natural-log LSE, or the fp32 partial + log2 LSE of partition p.
+// either the final output (bf16) + natural-log LSE, or an fp32 partial + log2 LSE: the row of
+// partition p, or, when spill_row0 >= 0, partial row spill_row0 + (row within the tile).
 template <int D, int NT>
 __device__ __forceinline__ void finish_wave(const DecodeArgs &a, int p, bool single, int lane,
-                                            const WaveRows<D, NT> &w, const WaveAcc<D, NT> &st) {
+                                            const WaveRows<D, NT> &w, const WaveAcc<D, NT> &st,
+                                            int64_t spill_row0 = -1) {
   constexpr int ND = D / 16;
   const int grp = lane >> 4;
   #pragma unroll
@@ -307,7 +314,8 @@ __device__ __forceinline__ void finish_wave(const DecodeArgs &a, int p, bool sin
       }
       if (grp == 0 && a.lse) a.lse[orow] = lse2 * kLn2;
     } else {
-      const int64_t prow = (int64_t)p * a.total_q * a.num_heads + orow;
+      const int64_t prow = spill_row0 >= 0 ? spill_row0 + n * 16 + (lane & 15)
+                                           : (int64_t)p * a.total_q * a.num_heads + orow;
       float *o = a.part_o + prow * D + 4 * grp;
       #pragma unroll
       for (int t = 0; t < ND; ++t) *reinterpret_cast<float4_t *>(o + t * 16) = st.acc[n][t] * inv;

@@ -30,7 +30,6 @@ constexpr int kBlockSize = 16;
 // A wave holds the page ids it visits in one register (64 lanes): a partition spans at most 64 pages
 // per wave of the 4-wave workgroup, or 64 pages in all when one wave attends a whole partition.
 constexpr int kMaxPartition = 64 * 4 * kBlockSize;
-constexpr int kMaxPartitionPersistent = 64 * kBlockSize;   // keeps the item count per sequence small
 
 int cu_count() {
   static int cached[64];
@@ -60,8 +59,11 @@ struct Plan {
   int schedule;      // PKV_SCHEDULE_GRID / PKV_SCHEDULE_PERSISTENT
   int part_size;
   int num_parts;
+  int grid;          // persistent schedule: workgroups (a multiple of 8)
+  int64_t part_rows; // partial rows: num_parts * total_q * num_heads, plus the spill rows
+  int64_t spill_base;
   bool need_q_start;
-  size_t off_q_start, off_part_lse, off_part_o, bytes;
+  size_t off_q_start, off_item_pre, off_part_lse, off_part_o, bytes;
 };
 
 int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
@@ -86,9 +88,11 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
 // Policy.  Kernel: the matrix-core kernel for bf16, the vector-ALU kernel for fp32 (or when asked).
 // Rows per tile: the whole GQA group times the new tokens when it fits the kernel, else tiles.
 // Schedule: persistent for the matrix-core kernel when its limits allow, else the grid.  Partition
-// size: 512 keys for the persistent schedule; for the grid schedules the largest of 512/256/128/64
-// keys that still gives about 2048 live workgroups (8 per CU) for a mean context of half the
-// maximum.  No split at all when the whole context fits one partition.
+// size: the persistent schedule balances the page stream over its waves by itself and splits a work
+// item wherever a share boundary falls, so it takes no partitions of its own unless asked (a given
+// size is rounded up to whole ring cycles, 64 keys); the grid schedules take the largest of
+// 512/256/128/64 keys that still gives about 2048 live workgroups (8 per CU) for a mean context of
+// half the maximum.  No split at all when the whole context fits one partition.
 Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
                int num_kv_heads, int head_dim, int dtype, bool ragged_q,
                const pkv_decode_options *opts) {
@@ -108,17 +112,20 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   pl.rows_per_tile = R;
   pl.row_tiles = ceil_div(rows, R);
   const int asked_sched = opts ? opts->schedule : 0;
-  const bool can_persist = pl.path == PKV_PATH_MFMA && num_seqs <= pkv::persistent_max_seqs();
+  // the stream of one kv head is counted in int
+  const int64_t stream_pages = (int64_t)num_seqs * pl.row_tiles * ceil_div(max_context_len, kBlockSize);
+  const bool can_persist = pl.path == PKV_PATH_MFMA && num_seqs <= pkv::persistent_max_seqs() &&
+                           stream_pages * num_kv_heads < ((int64_t)1 << 31);
   pl.schedule = (asked_sched == PKV_SCHEDULE_GRID || !can_persist) ? PKV_SCHEDULE_GRID : PKV_SCHEDULE_PERSISTENT;
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
   pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth
                                             : pkv::mfma_default_depth(head_dim, R, persist);
   if (persist && pl.depth == 3) pl.depth = 4;   // the persistent ring depth must divide 4
   int P = opts ? opts->partition_size : 0;
-  if (P == 0 && persist) {
-    // a wave streams whole runs of partitions, so small partitions only add partials to merge;
-    // 512 keys measured best for 32x8 short, 256x8 long and 32x8x5-row verify batches
-    P = 512;
+  const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
+  if (persist) {
+    if (P == 0 || P > whole) P = whole;
+    P = ceil_div(P, 4 * kBlockSize) * 4 * kBlockSize;
   } else if (P == 0) {
     const int64_t units1 = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
     const int64_t mean_ctx = (max_context_len + 1) / 2;
@@ -130,26 +137,35 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
       }
     }
   }
-  const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
-  if (P >= whole) P = whole;
-  if (P > kMaxPartition) P = kMaxPartition;
-  if (persist) {
-    // whole ring cycles per partition: a multiple of 64 keys (4 pages), at most 1024
-    P = ceil_div(P, 4 * kBlockSize) * 4 * kBlockSize;
-    if (P > kMaxPartitionPersistent) P = kMaxPartitionPersistent;
+  if (!persist) {
+    if (P >= whole) P = whole;
+    if (P > kMaxPartition) P = kMaxPartition;
   }
   pl.part_size = P;
   pl.num_parts = ceil_div(max_context_len, P);
+  pl.grid = 0;
+  pl.spill_base = -1;
+  pl.part_rows = pl.num_parts > 1 ? (int64_t)pl.num_parts * total_q * num_heads : 0;
+  if (persist) {
+    // every wave of the grid owns rows_per_tile spill rows after the partition rows
+    const int per_cu = pkv::mfma_persistent_wgs_per_cu(head_dim, R, pl.depth, num_seqs);
+    pl.grid = cu_count() * per_cu / 8 * 8;
+    if (pl.grid < 8) pl.grid = 8;
+    pl.spill_base = (int64_t)pl.num_parts * total_q * num_heads;
+    pl.part_rows = pl.spill_base + (int64_t)pl.grid * 4 * R;
+  }
   pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
   size_t off = 0;
   pl.off_q_start = off;
   if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
+  pl.off_item_pre = off;
+  if (persist) off = align_up(off + (size_t)(num_seqs + 1) * 4);
   pl.off_part_lse = off;
   pl.off_part_o = off;
-  if (pl.num_parts > 1) {
-    off = align_up(off + (size_t)pl.num_parts * total_q * num_heads * 4);
+  if (pl.part_rows > 0) {
+    off = align_up(off + (size_t)pl.part_rows * 4);
     pl.off_part_o = off;
-    off = align_up(off + (size_t)pl.num_parts * total_q * num_heads * head_dim * 4);
+    off = align_up(off + (size_t)pl.part_rows * head_dim * 4);
   }
   pl.bytes = off;
   return pl;
@@ -215,10 +231,7 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   info->rows_per_tile = pl.rows_per_tile;
   info->row_tiles = pl.row_tiles;
   info->pipeline_depth = pl.depth;
-  info->grid_waves = pl.schedule == PKV_SCHEDULE_PERSISTENT
-                         ? cu_count() * pkv::mfma_persistent_wgs_per_cu(head_dim, pl.rows_per_tile, pl.depth,
-                                                                         num_seqs) * 4
-                         : 0;
+  info->grid_waves = pl.grid * 4;
   info->schedule = pl.schedule;
   info->workspace_bytes = pl.bytes;
   return PKV_OK;
@@ -260,8 +273,15 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   a.q_start = pl.need_q_start ? reinterpret_cast<const int32_t *>(ws + pl.off_q_start) : nullptr;
   a.out = out;
   a.lse = lse;
-  a.part_lse = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
-  a.part_o = pl.num_parts > 1 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
+  a.part_lse = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
+  a.part_o = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
+  const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
+  a.item_pre = persist ? reinterpret_cast<int32_t *>(ws + pl.off_item_pre) : nullptr;
+  a.spill_base = pl.spill_base;
+  a.share_waves = pl.grid / 8 * 4;
+  // share boundaries must start ring cycles only where a partition end could fall inside a run
+  a.cut_align = pl.num_parts > 1 ? pl.depth : 1;
+  a.rows_per_tile = pl.rows_per_tile;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -287,19 +307,15 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   if (opts && opts->event_main_begin &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_begin), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
-  int grid = 0;
-  if (pl.schedule == PKV_SCHEDULE_PERSISTENT)
-    grid = cu_count() * pkv::mfma_persistent_wgs_per_cu(head_dim, pl.rows_per_tile, pl.depth, num_seqs);
   const hipError_t le =
       pl.path == PKV_PATH_MFMA
-          ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, pl.depth,
-                                    pl.schedule == PKV_SCHEDULE_PERSISTENT, grid, s)
+          ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, pl.depth, persist, pl.grid, s)
           : pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s);
   if (le != hipSuccess) return PKV_ERR_LAUNCH;
   if (opts && opts->event_main_end &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_end), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
-  if (pl.num_parts > 1) {
+  if (pl.num_parts > 1 || persist) {
     if (pkv::launch_combine(a, bf16, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
   }
   return PKV_OK;

@@ -82,12 +82,26 @@ def test_decode_argument_validation(lib):
 
 def test_workspace_and_partition_policy(lib):
     o = _lib.DecodeOptions(0, 0, 0, 0, None, None)
-    # long contexts split into 512-key partitions with fp32 partials
     info = _lib.DecodePlanInfo()
+    # bf16 goes to the persistent matrix-core schedule, which takes no partitions of its own: one
+    # partition per sequence, plus spill rows (rows_per_tile per wave of its grid) for cut pieces
     assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o), ctypes.byref(info)) == 0
-    assert info.partition_size == 512 and info.num_partitions == 64
+    assert info.partition_size == 32768 and info.num_partitions == 1
+    assert info.schedule == _lib.SCHEDULE_PERSISTENT and info.grid_waves % 32 == 0 and info.grid_waves > 0
     assert info.path == _lib.PATH_MFMA and info.rows_per_tile == 16 and info.row_tiles == 1
     ws = lib.pkv_decode_workspace_bytes(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o))
+    assert ws >= (256 * 64 + info.grid_waves * 16) * (128 + 1) * 4 + 257 * 4
+    # asked-for 512-key partitions (rounded to whole ring cycles: 64 keys) on top of that
+    o512 = _lib.DecodeOptions(500, 0, 0, 0, None, None)
+    assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o512), ctypes.byref(info)) == -3
+    o512 = _lib.DecodeOptions(512, 0, 0, 0, None, None)
+    assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(o512), ctypes.byref(info)) == 0
+    assert info.partition_size == 512 and info.num_partitions == 64
+    # the grid schedule picks 512-key partitions for this batch and needs only the partials
+    og = _lib.DecodeOptions(0, 0, 0, _lib.SCHEDULE_GRID, None, None)
+    assert lib.pkv_decode_plan(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(og), ctypes.byref(info)) == 0
+    assert info.partition_size == 512 and info.num_partitions == 64 and info.grid_waves == 0
+    ws = lib.pkv_decode_workspace_bytes(256, 256, 1, 32768, 64, 8, 128, 1, ctypes.byref(og))
     assert ws >= 64 * 256 * 64 * (128 + 1) * 4
     # a context that fits one partition needs no partials
     o1 = _lib.DecodeOptions(4096, 0, 0, 0, None, None)

@@ -91,7 +91,8 @@ def test_spec_verify(gpu_lib):
 
 def test_long_context_splitk_sampled(gpu_lib):
     """Full-size long-context workload in the benchmark's launch configuration (512-key partitions),
-    checked on sampled sequences: the longest, the shortest and a seeded spread."""
+    and with the persistent schedule's own balanced split, checked on sampled sequences: the longest,
+    the shortest and a seeded spread."""
     w = W.build(4, DEV)
     order = np.argsort(w.context_lens)
     rng = np.random.default_rng(5)
@@ -101,14 +102,55 @@ def test_long_context_splitk_sampled(gpu_lib):
     rows = np.zeros(w.total_q, dtype=bool)
     rows[seqs] = True
     _say(f"   seqs {seqs} ctx {[int(w.context_lens[s]) for s in seqs]}")
-    for path, sched in _paths(w):
-        _say(f"[case] long_ctx_splitk_bf16 P=512 (full size) path={path} schedule={sched}")
-        out, lse = run_library(w, DEV, partition_size=512, path=path, schedule=sched)
+    for (path, sched), P in [(v, 512) for v in _paths(w)] + [(MFMA_PERSIST, 0)]:
+        _say(f"[case] long_ctx_splitk_bf16 P={P} (full size) path={path} schedule={sched}")
+        out, lse = run_library(w, DEV, partition_size=P, path=path, schedule=sched)
         d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, rows=rows)
         _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
         assert d_out <= BF16_TOL and d_lse <= LSE_TOL
         # a property that holds for every row, sampled or not: finite output and LSE
         assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def _check_persistent(w, P, depth):
+    _say(f"[case] {w.spec.name} persistent P={P} depth={depth}")
+    out, lse = run_library(w, DEV, partition_size=P, path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT,
+                           depth=depth)
+    ref_out, ref_lse = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+    assert np.isfinite(d_out) and d_out <= BF16_TOL
+    assert np.isfinite(d_lse) and d_lse <= LSE_TOL
+
+
+@pytest.mark.parametrize("depth", [2, 4])
+def test_balanced_split_one_long_sequence(gpu_lib, depth):
+    """One 32768-token sequence on one kv head: each wave of the persistent grid gets about one page,
+    so the sequence is cut into hundreds of pieces (more than 64 merge sources per row) and many
+    shares end up empty after their boundaries move to ring-cycle starts."""
+    w = W.build(W.custom("one_long", [32768], num_heads=8, num_kv_heads=1, head_dim=128), DEV)
+    for P in (0, 512):
+        _check_persistent(w, P, depth)
+
+
+def test_balanced_split_many_short_sequences(gpu_lib):
+    """600 short ragged sequences: most work items lie inside one share (final output straight from
+    the partition kernel), the rest are cut at share boundaries."""
+    rng = np.random.default_rng(11)
+    ctx = rng.integers(1, 80, 600)
+    ql = np.minimum(rng.integers(1, 4, 600), ctx)
+    spec = W.custom("many_short", ctx.tolist(), q_len=ql.tolist(), num_heads=16, num_kv_heads=4, head_dim=64)
+    w = W.build(spec, DEV)
+    for depth in (2, 4):
+        _check_persistent(w, 0, depth)
+
+
+def test_balanced_split_several_row_tiles(gpu_lib):
+    """96 query rows per kv head (GQA 32, 3 new tokens): three 32-row tiles, each its own work item."""
+    spec = W.custom("row_tiles", [700, 40, 2000, 3], q_len=3, num_heads=64, num_kv_heads=2, head_dim=128)
+    w = W.build(spec, DEV)
+    for P in (0, 64):
+        _check_persistent(w, P, 4)
 
 
 EDGE_CTX = [1, 15, 16, 17, 511, 512, 513, 1024, 1025]
