@@ -10,14 +10,14 @@
 //  * grid: one 4-wave workgroup per (kv head, partition, sequence, row tile) of a dense grid sized from
 //    the host-known maxima; workgroups past a sequence's end exit at once.  The waves of a workgroup
 //    take every fourth page of the partition and merge through LDS.
-//  * persistent: a grid of a few workgroups per CU.  Every workgroup lists the live work items from
-//    context_lens into LDS (items are (kv head, sequence, row tile, partition), kv-head-major), the
-//    8 XCDs take equal contiguous shares of the list, and every wave is an independent worker that
-//    takes an equal contiguous share of its XCD's items.  Consecutive partitions of one sequence in
-//    that share form one page stream (the softmax state is flushed at each partition boundary), so
-//    the page pipeline restarts only when the sequence changes.  No workgroup is spent on an empty
-//    partition, ragged lengths spread evenly over all waves, and the items that read one kv head's
-//    pages (including prefix pages several sequences share) stay under one L2.
+//  * persistent: a grid of a few workgroups per CU.  Every workgroup lists, from context_lens, the
+//    pages every work item (kv head, sequence, row tile) reads as one stream, kv-head-major; each
+//    wave is an independent worker that takes an equal contiguous share of that stream (each XCD
+//    one eighth).  A share boundary inside a work item cuts it into pieces, merged like partitions
+//    by the combine kernel, so every wave streams the same number of pages whatever the mix of
+//    lengths, the page pipeline restarts only where the sequence changes, and the items that read
+//    one kv head's pages (including prefix pages several sequences share) stay under one L2.
+//    Fixed partitions are optional here: when asked for, pieces also end at partition boundaries.
 #include "mfma_wave.h"
 
 namespace pkv {

@@ -72,7 +72,7 @@ NAMED: List[Spec] = [
     Spec("spec_verify_bf16", 32, 32, 8, 128, "bf16", ctx=("uniform", 512, 8192), q_len=5,
          seed=1003),
     Spec("long_ctx_splitk_bf16", 256, 64, 8, 128, "bf16", ctx=("lognormal", 4096, 0.8, 64, 32768),
-         partition_size=512, seed=1004),
+         seed=1004),
 ]
 
 

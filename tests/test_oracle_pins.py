@@ -217,6 +217,52 @@ def test_p8_shared_prefix_blocks_equal_private_copies():
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
+def test_p9_brute_force_scalar_loops_on_tiny_pool():
+    """Brute force on a tiny ragged case: every score, softmax weight and output element with Python
+    floats and math.exp, indexing the flat pool buffer directly (offset = ((block * KVH + kv head) *
+    B + slot) * D + d for K, ((block * KVH + kv head) * D + d) * B + slot for V)."""
+    rng = np.random.default_rng(19)
+    B, KVH, G, D = 16, 2, 2, 8
+    H = KVH * G
+    ctx, ql = [1, 7, 16, 33], [1, 2, 1, 3]
+    pool = 10
+    kc = rng.standard_normal((pool, KVH, B, D)).astype(np.float32)
+    vc = rng.standard_normal((pool, KVH, D, B)).astype(np.float32)
+    perm = rng.permutation(pool)
+    table = np.full((4, 3), -1, dtype=np.int32)
+    used = 0
+    for s, n in enumerate(ctx):
+        for j in range(-(-n // B)):
+            table[s, j] = perm[used]
+            used += 1
+    q = rng.standard_normal((sum(ql), H, D)).astype(np.float32)
+    scale = 0.4
+    out, lse = O.paged_decode_attention(q, kc, vc, table, np.array(ctx), np.array(ql), scale, KVH, B)
+    kf, vf = kc.reshape(-1).tolist(), vc.reshape(-1).tolist()
+    row = 0
+    for s, n in enumerate(ctx):
+        for i in range(ql[s]):
+            for h in range(H):
+                g = h // G
+                xs = []
+                for t in range(n - ql[s] + i + 1):
+                    blk, slot = int(table[s, t // B]), t % B
+                    kbase = ((blk * KVH + g) * B + slot) * D
+                    xs.append(scale * sum(float(q[row, h, d]) * kf[kbase + d] for d in range(D)))
+                m = max(xs)
+                ws = [math.exp(x - m) for x in xs]
+                z = sum(ws)
+                assert abs(lse[row, h] - (m + math.log(z))) <= 1e-12
+                for d in range(D):
+                    o = 0.0
+                    for t, wt in enumerate(ws):
+                        blk, slot = int(table[s, t // B]), t % B
+                        o += wt / z * vf[((blk * KVH + g) * D + d) * B + slot]
+                    assert abs(out[row, h, d] - o) <= 1e-12
+            row += 1
+
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.uint16])
 def test_p10_cache_write_moves_bits_to_flat_offsets(dtype):
     rng = np.random.default_rng(19)
