@@ -200,6 +200,7 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--depth", type=int, default=0, help="MFMA register ring depth (0: policy)")
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
+    ap.add_argument("--wgs-per-cu", type=int, default=0, help="persistent grid: workgroups per CU (0: policy)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
     ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
@@ -247,7 +248,7 @@ def main():
     code = _lib.PKV_BF16 if spec.dtype == "bf16" else _lib.PKV_F32
     sched = {"auto": 0, "grid": 1, "persistent": 2}[args.schedule]
     plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, P, path,
-                            args.depth, sched)
+                            args.depth, sched, args.wgs_per_cu)
     P_used = plan["partition_size"]
     kernel = "decode_valu_kernel"
     if plan["path"] == _lib.PATH_MFMA:
@@ -280,7 +281,8 @@ def main():
                             H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
                             partition_size=P, path=path, depth=args.depth, schedule=sched, workspace=ws,
                             new_k=w.new_k, new_v=w.new_v,
-                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None else None)
+                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None else None,
+                            wgs_per_cu=args.wgs_per_cu)
 
     def step(i, events=None):
         r = i % R
@@ -362,7 +364,8 @@ def main():
             "head_dim": D, "block_size": spec.block_size, "q_len": w.max_q_len,
             "context_tokens": tokens, "max_context_len": w.max_context_len, "partition_size": P_used,
             "path": kernel.split("_")[1], "schedule": sched_name,
-            "pipeline_depth": plan["pipeline_depth"], "pool_copies": R, "appends_new_token": w.slot_mapping is not None,
+            "pipeline_depth": plan["pipeline_depth"], "grid_waves": plan["grid_waves"], "pool_copies": R,
+            "appends_new_token": w.slot_mapping is not None,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

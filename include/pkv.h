@@ -86,6 +86,8 @@ typedef struct pkv_decode_options {
   int schedule;             /* pkv_schedule */
   void *event_main_begin;   /* hipEvent_t recorded on `stream` right before the partition kernel */
   void *event_main_end;     /* hipEvent_t recorded right after it (before the combine kernel) */
+  int workgroups_per_cu;    /* persistent schedule: resident workgroups per CU, at most what fits
+                               (0 = policy) */
 } pkv_decode_options;
 
 /*

@@ -25,7 +25,8 @@ _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
 class DecodeOptions(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("path", _c_int), ("pipeline_depth", _c_int),
-                ("schedule", _c_int), ("event_main_begin", _vp), ("event_main_end", _vp)]
+                ("schedule", _c_int), ("event_main_begin", _vp), ("event_main_end", _vp),
+                ("workgroups_per_cu", _c_int)]
 
 
 class DecodePlanInfo(ctypes.Structure):
@@ -94,8 +95,9 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _opts(partition_size: int, path: int, events, depth: int = 0, schedule: int = 0) -> DecodeOptions:
-    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
+def _opts(partition_size: int, path: int, events, depth: int = 0, schedule: int = 0,
+          wgs_per_cu: int = 0) -> DecodeOptions:
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
     if events is not None:
         b, e = events
         o.event_main_begin = b.cuda_event
@@ -124,8 +126,8 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 def decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                            head_dim, dtype_code, partition_size=0, path=PATH_AUTO, depth=0,
-                           schedule=0) -> int:
-    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
+                           schedule=0, wgs_per_cu=0) -> int:
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
     return int(load().pkv_decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads,
                                                  num_kv_heads, head_dim, dtype_code, ctypes.byref(o)))
 
@@ -136,9 +138,9 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
-                dtype_code, partition_size=0, path=PATH_AUTO, depth=0, schedule=0) -> dict:
+                dtype_code, partition_size=0, path=PATH_AUTO, depth=0, schedule=0, wgs_per_cu=0) -> dict:
     """What the library launches for these sizes: partition size, kernel path, row tiling, workspace."""
-    o = DecodeOptions(partition_size, path, depth, schedule, None, None)
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
     info = DecodePlanInfo()
     rc = int(load().pkv_decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                                     head_dim, dtype_code, ctypes.byref(o), ctypes.byref(info)))
@@ -164,7 +166,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       num_heads: int, num_kv_heads: int, head_dim: int, block_size: int, scale: float,
                       max_context_len: int, max_q_len: int = 1, partition_size: int = 0,
                       path: int = PATH_AUTO, workspace: Optional[torch.Tensor] = None,
-                      events=None, stream=None, depth: int = 0, schedule: int = 0) -> None:
+                      events=None, stream=None, depth: int = 0, schedule: int = 0,
+                      wgs_per_cu: int = 0) -> None:
     """Decode attention through the C ABI.  q/out [total_q, H, D]; lse fp32 [total_q, H] or None.
 
     q_lens None means every sequence has max_q_len new tokens.  max_context_len is a host-known upper
@@ -191,7 +194,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
               "lse: fp32 [total_q, H]")
     code = _dtype_code(q)
-    o = _opts(partition_size, path, events, depth, schedule)
+    o = _opts(partition_size, path, events, depth, schedule, wgs_per_cu)
     need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                               num_kv_heads, head_dim, code, ctypes.byref(o)))
     if workspace is None and need > 0:
@@ -215,7 +218,7 @@ class DecodeStep:
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
                  num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len=1,
                  partition_size=0, path=PATH_AUTO, depth=0, schedule=0, workspace=None,
-                 new_k=None, new_v=None, slot_mapping=None):
+                 new_k=None, new_v=None, slot_mapping=None, wgs_per_cu=0):
         lib = load()
         self._lib = lib
         total_q = q.shape[0]
@@ -238,8 +241,8 @@ class DecodeStep:
             _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads)
                   and lse.is_contiguous(), "lse: fp32 [total_q, H]")
         code = _dtype_code(q)
-        self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None)
-        self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None)
+        self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
+        self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
         need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                                   num_kv_heads, head_dim, code, ctypes.byref(self._opts)))
         if workspace is None and need > 0:

@@ -250,9 +250,10 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
 // Rows one launch covers per work item: 16 per N tile, at most two N tiles.
 int mfma_rows_per_tile(int rows) { return rows > 16 ? 32 : 16; }
 
-// Pages in flight per wave = depth - 1.  Depths 2..4 are built for the grid schedule; the persistent
-// schedule streams runs of partitions and takes depths that divide the pages of a partition (2, 4).
-int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent) { return persistent ? 4 : 3; }
+// Pages in flight per wave = depth - 1.  Depths 2..4 are built for both schedules; with fixed
+// partitions the persistent schedule takes depths that divide the 4-page granule of a partition (2, 4).
+// Persistent default: depth 2 (measured best with one workgroup per CU on all five workloads).
+int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent) { return persistent ? 2 : 3; }
 
 // Largest batch the persistent schedule lists in LDS, and the LDS it needs.
 int persistent_max_seqs() { return 4096; }
@@ -263,8 +264,10 @@ static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent
                                  hipStream_t st) {
   if (persistent) {
     const int g = grid;
-    if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2><<<g, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
-    else decode_mfma_persistent_kernel<D, NT, 4><<<g, 256, persistent_lds_bytes(a.num_seqs), st>>>(a);
+    const size_t lds = persistent_lds_bytes(a.num_seqs);
+    if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2><<<g, 256, lds, st>>>(a);
+    else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3><<<g, 256, lds, st>>>(a);
+    else decode_mfma_persistent_kernel<D, NT, 4><<<g, 256, lds, st>>>(a);
     return hipGetLastError();
   }
   switch (depth) {
@@ -287,7 +290,8 @@ static int occupancy_of(int num_seqs) {
 
 template <int D, int NT>
 static int occupancy_dn(int depth, int num_seqs) {
-  return depth == 2 ? occupancy_of<D, NT, 2>(num_seqs) : occupancy_of<D, NT, 4>(num_seqs);
+  return depth == 2 ? occupancy_of<D, NT, 2>(num_seqs)
+                    : depth == 3 ? occupancy_of<D, NT, 3>(num_seqs) : occupancy_of<D, NT, 4>(num_seqs);
 }
 
 // Cached per (head_dim, N tiles, depth) and per LDS size class (the tables grow with the batch).

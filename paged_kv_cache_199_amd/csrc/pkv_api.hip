@@ -81,6 +81,7 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
     if (opts->pipeline_depth != 0 && (opts->pipeline_depth < 2 || opts->pipeline_depth > 4))
       return PKV_ERR_UNSUPPORTED;
     if (opts->schedule < 0 || opts->schedule > PKV_SCHEDULE_PERSISTENT) return PKV_ERR_UNSUPPORTED;
+    if (opts->workgroups_per_cu < 0) return PKV_ERR_UNSUPPORTED;
   }
   return PKV_OK;
 }
@@ -120,7 +121,6 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
   pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth
                                             : pkv::mfma_default_depth(head_dim, R, persist);
-  if (persist && pl.depth == 3) pl.depth = 4;   // the persistent ring depth must divide 4
   int P = opts ? opts->partition_size : 0;
   const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
   if (persist) {
@@ -143,12 +143,18 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   }
   pl.part_size = P;
   pl.num_parts = ceil_div(max_context_len, P);
+  // with fixed partitions, persistent share boundaries fall on ring cycles that must tile 4 pages
+  if (persist && pl.num_parts > 1 && pl.depth == 3) pl.depth = 4;
   pl.grid = 0;
   pl.spill_base = -1;
   pl.part_rows = pl.num_parts > 1 ? (int64_t)pl.num_parts * total_q * num_heads : 0;
   if (persist) {
     // every wave of the grid owns rows_per_tile spill rows after the partition rows
-    const int per_cu = pkv::mfma_persistent_wgs_per_cu(head_dim, R, pl.depth, num_seqs);
+    // one workgroup per CU unless asked: fewer, longer shares measured faster than a full CU of
+    // waves (less per-wave start-up and fewer cut pieces to merge) on all five workloads
+    const int fits = pkv::mfma_persistent_wgs_per_cu(head_dim, R, pl.depth, num_seqs);
+    const int asked_wgs = opts ? opts->workgroups_per_cu : 0;
+    const int per_cu = asked_wgs > 0 ? (asked_wgs < fits ? asked_wgs : fits) : 1;
     pl.grid = cu_count() * per_cu / 8 * 8;
     if (pl.grid < 8) pl.grid = 8;
     pl.spill_base = (int64_t)pl.num_parts * total_q * num_heads;
