@@ -205,6 +205,9 @@ def main():
     ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
     ap.add_argument("--no-graph", action="store_true", help="time the eager step only")
+    ap.add_argument("--append", default="fused", choices=["fused", "slots"],
+                    help="appending workloads: write the new tokens inside the decode call (fused) or "
+                         "with pkv_kv_cache_write through slot_mapping first (slots)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -281,8 +284,8 @@ def main():
                             H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
                             partition_size=P, path=path, depth=args.depth, schedule=sched, workspace=ws,
                             new_k=w.new_k, new_v=w.new_v,
-                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None else None,
-                            wgs_per_cu=args.wgs_per_cu)
+                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None and args.append == "slots"
+                            else None, wgs_per_cu=args.wgs_per_cu)
 
     def step(i, events=None):
         r = i % R
@@ -366,6 +369,7 @@ def main():
             "path": kernel.split("_")[1], "schedule": sched_name,
             "pipeline_depth": plan["pipeline_depth"], "grid_waves": plan["grid_waves"], "pool_copies": R,
             "appends_new_token": w.slot_mapping is not None,
+            "append": (args.append if w.slot_mapping is not None else None),
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

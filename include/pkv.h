@@ -155,6 +155,30 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
                           float scale, int dtype, const pkv_decode_options *opts,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * One decode step with its append: the new tokens' K/V rows are written into their cache slots and
+ * attended in the same call (the step a serving engine runs once per generated token; inferd
+ * follow-up plan: the block allocator feeding live decode).  new_k / new_v: [total_q, num_kv_heads,
+ * head_dim] of `dtype`, packed like q (row qbase_s + i is new token i of sequence s).  Token i of
+ * sequence s goes to position p = context_lens[s] - q_lens[s] + i, i.e. block
+ * block_tables[s][p / block_size], offset p % block_size (its slot is block * block_size + offset,
+ * the slot_mapping a caller of pkv_kv_cache_write would pass).  The result equals
+ * pkv_kv_cache_write with those slots followed by pkv_paged_attn_decode, bit for bit.  The matrix-core
+ * persistent schedule does both in one pass for up to 8 new tokens per sequence; other launches run
+ * a small append kernel first.  Extra precondition: no other sequence of the batch reads the new
+ * tokens' slots (a block shared by several sequences is copied before it is appended to).  Other
+ * arguments, preconditions and errors as pkv_paged_attn_decode; new_k / new_v NULL -> PKV_ERR_NULL.
+ */
+int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *new_v,
+                                 void *k_cache, void *v_cache,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *q_lens, void *out, float *lse,
+                                 int num_seqs, int max_blocks_per_seq, int total_q, int max_q_len,
+                                 int max_context_len, int64_t num_blocks,
+                                 int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                 float scale, int dtype, const pkv_decode_options *opts,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable text for a pkv_status value (static storage). */
 const char *pkv_status_string(int status);
 

@@ -45,6 +45,10 @@ EXPORTS = {
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                        _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                        ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
+    "pkv_paged_attn_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                              _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
+                                              ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
     "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_version": (_c_int, []),
@@ -167,8 +171,12 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       max_context_len: int, max_q_len: int = 1, partition_size: int = 0,
                       path: int = PATH_AUTO, workspace: Optional[torch.Tensor] = None,
                       events=None, stream=None, depth: int = 0, schedule: int = 0,
-                      wgs_per_cu: int = 0) -> None:
+                      wgs_per_cu: int = 0, new_k: Optional[torch.Tensor] = None,
+                      new_v: Optional[torch.Tensor] = None) -> None:
     """Decode attention through the C ABI.  q/out [total_q, H, D]; lse fp32 [total_q, H] or None.
+
+    With new_k / new_v ([total_q, KVH, D], packed like q) the step appends them first, at each
+    sequence's last q positions through its block table (pkv_paged_attn_decode_append).
 
     q_lens None means every sequence has max_q_len new tokens.  max_context_len is a host-known upper
     bound of context_lens (the kernels never read device data on the host).  A workspace tensor
@@ -200,17 +208,31 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if workspace is None and need > 0:
         workspace = new_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                   _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),
-                                   S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB,
-                                   num_heads, num_kv_heads, head_dim, block_size, float(scale), code,
-                                   ctypes.byref(o), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(rc, "pkv_paged_attn_decode")
+    if new_k is None:
+        rc = lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                       _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),
+                                       S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB,
+                                       num_heads, num_kv_heads, head_dim, block_size, float(scale), code,
+                                       ctypes.byref(o), _ptr(workspace), ws_bytes, _stream(stream))
+        _check(rc, "pkv_paged_attn_decode")
+        return
+    _need(new_v is not None and new_k.shape == new_v.shape
+          and tuple(new_k.shape) == (total_q, num_kv_heads, head_dim), "new_k / new_v must be [total_q, KVH, D]")
+    for t in (new_k, new_v):
+        _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, contiguous, GPU")
+    rc = lib.pkv_paged_attn_decode_append(_ptr(q), _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(block_tables), _ptr(context_lens), _ptr(q_lens), _ptr(out),
+                                          _ptr(lse), S, block_tables.shape[1], total_q, max_q_len,
+                                          max_context_len, NB, num_heads, num_kv_heads, head_dim, block_size,
+                                          float(scale), code, ctypes.byref(o), _ptr(workspace), ws_bytes,
+                                          _stream(stream))
+    _check(rc, "pkv_paged_attn_decode_append")
 
 
 class DecodeStep:
-    """One decode step bound once: the optional slot-mapped append of the new tokens' K/V, then paged
-    decode attention, with the same checks as kv_cache_write / paged_attn_decode done at
+    """One decode step bound once: the optional append of the new tokens' K/V (through slot_mapping
+    with pkv_kv_cache_write, or, given new_k / new_v without slot_mapping, in the decode call itself
+    with pkv_paged_attn_decode_append), then paged decode attention, with the same checks as kv_cache_write / paged_attn_decode done at
     construction.  A call only enqueues the two C calls on the current stream, so a serving loop
     pays little host time per step and the step can be captured in a HIP graph.  A call may swap in
     other cache tensors of the same shape, dtype and device (not checked again)."""
@@ -257,6 +279,14 @@ class DecodeStep:
                      num_heads, num_kv_heads, head_dim, block_size, float(scale), code)
         self._tail = (_ptr(workspace), ws_bytes)
         self._write = None
+        self._fused = None
+        if new_k is not None and slot_mapping is None:
+            _need(new_v is not None and new_k.shape == new_v.shape
+                  and tuple(new_k.shape) == (total_q, num_kv_heads, head_dim),
+                  "new_k / new_v must be [total_q, KVH, D] for the fused append")
+            for t in (new_k, new_v):
+                _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, on the GPU")
+            self._fused = (_ptr(new_k), _ptr(new_v))
         if slot_mapping is not None:
             T = new_k.shape[0]
             _need(new_k.dim() == 3 and new_k.shape == new_v.shape and tuple(new_k.shape[1:]) == (num_kv_heads, head_dim),
@@ -285,6 +315,12 @@ class DecodeStep:
             o = self._opts_ev
             o.event_main_begin = getattr(events[0], "cuda_event", events[0])
             o.event_main_end = getattr(events[1], "cuda_event", events[1])
+        if self._fused is not None:
+            rc = lib.pkv_paged_attn_decode_append(*self._head, *self._fused, kc, vc, *self._mid, ctypes.byref(o),
+                                                  *self._tail, st)
+            if rc != 0:
+                _check(rc, "pkv_paged_attn_decode_append")
+            return
         rc = lib.pkv_paged_attn_decode(*self._head, kc, vc, *self._mid, ctypes.byref(o), *self._tail, st)
         if rc != 0:
             _check(rc, "pkv_paged_attn_decode")

@@ -39,6 +39,10 @@ struct DecodeArgs {
   int share_waves;             // waves per XCD in the persistent grid
   int cut_align;               // share boundaries inside a work item fall on multiples of this
   int rows_per_tile;
+  // append in the same pass: the new tokens' K/V rows, [total_q, num_kv_heads, head_dim] packed like
+  // q; NULL when nothing is appended
+  const void *new_k;
+  const void *new_v;
 };
 
 // Per-unit sequence facts with the clamps that keep bad metadata memory-safe.

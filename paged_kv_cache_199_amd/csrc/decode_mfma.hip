@@ -131,9 +131,11 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // LDS tables of the persistent schedule, per sequence s: pre = stream pages of sequences < s (for
 // one kv head), ctx = clamped context length, qb = first q row, rts = row tiles, qs = clamped new
 // tokens.  Workgroup 0 also leaves pre in the workspace for the combine kernel.
-template <int D, int NT, int NBUF>
+template <int D, int NT, int NBUF, bool APPEND>
 __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs a) {
   constexpr int ROWS = 16 * NT;
+  constexpr int APP = 2 * AppendRows<D>::MAXQ * AppendRows<D>::CH;   // staging chunks per wave
+  __shared__ uint4 app_lds[APPEND ? 4 : 1][APPEND ? APP : 1];
   extern __shared__ int sh[];
   const int S = a.num_seqs;
   int *pre = sh;              // [S + 1]
@@ -232,17 +234,28 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     const int j0 = local - rt * nblk;
     const int run = (int)min((int64_t)(nblk - j0), k_end - k);
 
+    const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    // appending: does this run reach the new tokens (the sequence's last qs positions)?
+    const bool reach = APPEND && (j0 + run) * kBlock > si.ctx - si.qs;
+    AppendRows<D> ar;
+    if (reach) append_load<D>(a, si, kvh, lane, ar);
     WaveRows<D, NT> w;
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
     WaveAcc<D, NT> st;
     init_acc<D, NT>(st);
-    stream_pages<D, NT, NBUF>(a, si, kvh, a.block_tables + (int64_t)s * a.max_blocks_per_seq, j0, j0 + run,
-                              PP, lane, w, st, [&](int part, int first, int end) {
-                                const bool whole = first == 0 && end == nblk && si.nparts == 1;
-                                finish_wave<D, NT>(a, part, whole, lane, w, st,
-                                                   first % PP == 0 ? -1 : spill_row0);
-                                init_acc<D, NT>(st);
-                              });
+    stream_pages<D, NT, NBUF>(
+        a, si, kvh, bt_row, j0, j0 + run, PP, lane, w, st,
+        [&](int part, int first, int end) {
+          const bool whole = first == 0 && end == nblk && si.nparts == 1;
+          finish_wave<D, NT>(a, part, whole, lane, w, st, first % PP == 0 ? -1 : spill_row0);
+          init_acc<D, NT>(st);
+        },
+        [&](int j, uint4 *kr, uint2 *vr) {
+          if constexpr (APPEND) {
+            if (reach) append_patch<D>(j, lane, ar, app_lds[wave], kr, vr);
+          }
+        });
+    if (reach && rt == 0) append_store<D>(a, kvh, bt_row, j0, j0 + run, lane, ar);
     k += run;
   }
 }
@@ -265,9 +278,15 @@ static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent
   if (persistent) {
     const int g = grid;
     const size_t lds = persistent_lds_bytes(a.num_seqs);
-    if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2><<<g, 256, lds, st>>>(a);
-    else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3><<<g, 256, lds, st>>>(a);
-    else decode_mfma_persistent_kernel<D, NT, 4><<<g, 256, lds, st>>>(a);
+    if (a.new_k) {
+      if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2, true><<<g, 256, lds, st>>>(a);
+      else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3, true><<<g, 256, lds, st>>>(a);
+      else decode_mfma_persistent_kernel<D, NT, 4, true><<<g, 256, lds, st>>>(a);
+    } else {
+      if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2, false><<<g, 256, lds, st>>>(a);
+      else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3, false><<<g, 256, lds, st>>>(a);
+      else decode_mfma_persistent_kernel<D, NT, 4, false><<<g, 256, lds, st>>>(a);
+    }
     return hipGetLastError();
   }
   switch (depth) {
@@ -282,7 +301,7 @@ static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent
 template <int D, int NT, int NBUF>
 static int occupancy_of(int num_seqs) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_persistent_kernel<D, NT, NBUF>, 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_persistent_kernel<D, NT, NBUF, false>, 256,
                                                    persistent_lds_bytes(num_seqs)) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;

@@ -6,6 +6,7 @@
 // contiguous run, copied with 16-byte moves.  V pages are dim-major: element d of the row lands at
 // stride block_size, one element per lane.  The source rows are read together with the slot (they
 // do not depend on it), so the kernel waits for memory once before it stores.
+#include "decode_args.h"
 #include "device_common.h"
 
 namespace pkv {
@@ -40,6 +41,53 @@ __global__ __launch_bounds__(64) void kv_write_kernel(const void *__restrict__ k
   elem_t *vd = static_cast<elem_t *>(vc) + page * D * kBlock + off;
   #pragma unroll
   for (int e = 0; e < VPL; ++e) vd[(lane + 64 * e) * kBlock] = vv[e];
+}
+
+// Append for the decode paths that do not fold it into the attention pass: new token i of sequence s
+// (row qbase + i of k / v, packed like q) goes to position ctx - q_s + i, the page found through the
+// block table.  One 64-thread workgroup per (sequence, new token, kv head).
+template <int E, int D>
+__global__ __launch_bounds__(64) void kv_append_kernel(DecodeArgs a) {
+  using elem_t = typename std::conditional<E == 2, uint16_t, uint32_t>::type;
+  constexpr int ROWB = D * E;
+  constexpr int VPL = D / 64;
+  const int KVH = a.num_kv_heads;
+  const int64_t u = blockIdx.x;
+  const int h = (int)(u % KVH);
+  const int64_t t = u / KVH;
+  const int i = (int)(t % a.max_q_len);
+  const int s = (int)(t / a.max_q_len);
+  const SeqInfo si = load_seq(a, s);
+  if (i >= si.qs || si.ctx <= 0) return;
+  const int row_q = si.qbase + i;
+  if (row_q >= a.total_q) return;
+  const int pos = si.ctx - si.qs + i;
+  const int64_t bid = a.block_tables[(int64_t)s * a.max_blocks_per_seq + pos / kBlock];
+  if (bid < 0 || bid >= a.num_blocks) return;
+  const int lane = threadIdx.x;
+  const int64_t row = (int64_t)row_q * KVH + h;
+  const int64_t page = bid * KVH + h;
+  const int off = pos % kBlock;
+  const char *ks = static_cast<const char *>(a.new_k) + row * ROWB;
+  if (lane < ROWB / 16)
+    *reinterpret_cast<uint4 *>(static_cast<char *>(const_cast<void *>(a.k_cache)) + (page * kBlock + off) * ROWB +
+                               lane * 16) = *reinterpret_cast<const uint4 *>(ks + lane * 16);
+  const elem_t *vs = static_cast<const elem_t *>(a.new_v) + row * D;
+  elem_t *vd = static_cast<elem_t *>(const_cast<void *>(a.v_cache)) + page * D * kBlock + off;
+  #pragma unroll
+  for (int e = 0; e < VPL; ++e) vd[(lane + 64 * e) * kBlock] = vs[lane + 64 * e];
+}
+
+hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st) {
+  const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.num_kv_heads;
+  if (bf16) {
+    if (head_dim == 64) kv_append_kernel<2, 64><<<grid, 64, 0, st>>>(a);
+    else kv_append_kernel<2, 128><<<grid, 64, 0, st>>>(a);
+  } else {
+    if (head_dim == 64) kv_append_kernel<4, 64><<<grid, 64, 0, st>>>(a);
+    else kv_append_kernel<4, 128><<<grid, 64, 0, st>>>(a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,

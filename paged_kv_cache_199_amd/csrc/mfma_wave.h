@@ -222,11 +222,11 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 // (the block table is read-only here): the id of the page issued NBUF steps later is fetched while
 // the current page is computed, so those loads never hold up the vector loads and a run of any
 // length streams without a restart.
-template <int D, int NT, int NBUF, class Flush>
+template <int D, int NT, int NBUF, class Flush, class Patch>
 __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
                                              const int32_t *bt_row, int jb, int je, int PP, int lane,
                                              const WaveRows<D, NT> &w, WaveAcc<D, NT> &st,
-                                             Flush flush) {
+                                             Flush flush, Patch patch) {
   constexpr int ROWB = D * 2;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
@@ -270,6 +270,7 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
       const int bn = (b + NBUF - 1) % NBUF;   // constants once the loop is unrolled
       issue(sid[b], kb[bn], vb[bn], okb[bn]);
       sid[b] = id_of(jb + j0 + b + 2 * NBUF - 1);
+      patch(jb + j0 + b, kb[b], vb[b]);
       mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
     }
     const int jl = jb + j0 + NBUF - 1;
@@ -280,9 +281,132 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   }
   if (j0 < n) {
     #pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b)
-      if (j0 + b < n) mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
+    for (int b = 0; b < NBUF - 1; ++b) {
+      if (j0 + b < n) {
+        patch(jb + j0 + b, kb[b], vb[b]);
+        mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
+      }
+    }
     flush(last / PP, piece, je);
+  }
+}
+
+// New tokens appended in the decode pass itself.  The q_s new tokens of a sequence sit at its last
+// positions ctx - q_s .. ctx - 1 (one or two pages).  A wave whose run reaches them loads their K/V
+// rows for its kv head into registers when it starts the run (those loads fly with the first
+// pages); on each page that holds new tokens it stages them through its LDS area and substitutes
+// them for the cache rows it just loaded (so no other wave's write has to come first); after the
+// run, row tile 0 stores them into their cache slots.  The K/V row of token i is row qbase + i of
+// new_k / new_v [total_q, KVH, D].
+template <int D>
+struct AppendRows {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  static constexpr int MAXQ = 8;                          // new tokens per sequence on this path
+  static constexpr int PER_LANE = (MAXQ * CH + 63) / 64;
+  uint4 k[PER_LANE];
+  uint4 v[PER_LANE];
+  int first;       // position of new token 0
+  int n;           // new tokens
+  bool staged;
+};
+
+template <int D>
+__device__ __forceinline__ void append_load(const DecodeArgs &a, const SeqInfo &si, int kvh, int lane,
+                                            AppendRows<D> &r) {
+  constexpr int CH = AppendRows<D>::CH;
+  r.first = si.ctx - si.qs;
+  r.n = min(si.qs, AppendRows<D>::MAXQ);   // more new tokens than that is a broken precondition
+  r.staged = false;
+  const char *nk = static_cast<const char *>(a.new_k);
+  const char *nv = static_cast<const char *>(a.new_v);
+  #pragma unroll
+  for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+    const int c = lane + 64 * u;
+    const int tok = c / CH;
+    const bool ok = tok < r.n && si.qbase + tok < a.total_q;
+    const int64_t off = (((int64_t)(ok ? si.qbase + tok : 0) * a.num_kv_heads + kvh) * CH + c % CH) * 16;
+    r.k[u] = ok ? ld16(nk + off) : make_uint4(0, 0, 0, 0);
+    r.v[u] = ok ? ld16(nv + off) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Page j (logical) of the run: substitute the new tokens it holds for the cache rows just loaded.
+// lds: this wave's staging area, 2 * MAXQ * CH chunks.
+template <int D>
+__device__ __forceinline__ void append_patch(int j, int lane, AppendRows<D> &r, uint4 *lds, uint4 *kr,
+                                             uint2 *vr) {
+  constexpr int CH = AppendRows<D>::CH;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int p0 = j * kBlock;
+  if (p0 + kBlock <= r.first) return;                     // wave-uniform: no new token on this page
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  if (!r.staged) {
+    #pragma unroll
+    for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+      const int c = lane + 64 * u;
+      if (c < r.n * CH) {
+        lds[c] = r.k[u];
+        lds[AppendRows<D>::MAXQ * CH + c] = r.v[u];
+      }
+    }
+    wave_lds_sync();
+    r.staged = true;
+  }
+  const uint16_t *lv = reinterpret_cast<const uint16_t *>(lds + AppendRows<D>::MAXQ * CH);
+  const int kpos = p0 + col;
+  if (kpos >= r.first && kpos < r.first + r.n) {
+    const int tok = kpos - r.first;
+    #pragma unroll
+    for (int c = 0; c < NK; ++c) kr[c] = lds[tok * CH + c * 4 + grp];
+  }
+  #pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int vpos = p0 + 4 * grp + e;
+    if (vpos >= r.first && vpos < r.first + r.n) {
+      const int tok = vpos - r.first;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        const uint32_t x = lv[tok * D + col + 16 * t];
+        if (e == 0) vr[t].x = (vr[t].x & 0xffff0000u) | x;
+        else if (e == 1) vr[t].x = (vr[t].x & 0x0000ffffu) | (x << 16);
+        else if (e == 2) vr[t].y = (vr[t].y & 0xffff0000u) | x;
+        else vr[t].y = (vr[t].y & 0x0000ffffu) | (x << 16);
+      }
+    }
+  }
+}
+
+// After the run: store the new tokens that live on its pages [jb, je) into their cache slots (row
+// tile 0 only, so each slot is written once).  Stores wait until the page loads are done: on this
+// chip they share the counter the page ring waits on.
+template <int D>
+__device__ __forceinline__ void append_store(const DecodeArgs &a, int kvh, const int32_t *bt_row, int jb, int je,
+                                             int lane, const AppendRows<D> &r) {
+  constexpr int CH = AppendRows<D>::CH;
+  constexpr int ROWB = AppendRows<D>::ROWB;
+  char *kc = static_cast<char *>(const_cast<void *>(a.k_cache));
+  uint16_t *vc = static_cast<uint16_t *>(const_cast<void *>(a.v_cache));
+  #pragma unroll
+  for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+    const int c = lane + 64 * u;
+    const int tok = c / CH;
+    const int pos = r.first + tok;
+    const int j = pos / kBlock;
+    if (tok < r.n && j >= jb && j < je) {
+      const int64_t bid = bt_row[j];
+      if (bid >= 0 && bid < a.num_blocks) {
+        const int cc = c % CH;
+        const int off = pos - j * kBlock;
+        const int64_t page = bid * a.num_kv_heads + kvh;
+        *reinterpret_cast<uint4 *>(kc + (page * kBlock + off) * ROWB + cc * 16) = r.k[u];
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&r.v[u]);
+        #pragma unroll
+        for (int q = 0; q < 8; ++q) vc[(page * D + cc * 8 + q) * kBlock + off] = e[q];
+      }
+    }
   }
 }
 

@@ -21,6 +21,7 @@ int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent);
 int persistent_max_seqs();
 int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs);
 hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
+hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 }  // namespace pkv
 
@@ -243,13 +244,17 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   return PKV_OK;
 }
 
-int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
-                          const int32_t *block_tables, const int32_t *context_lens,
-                          const int32_t *q_lens, void *out, float *lse, int num_seqs,
-                          int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
-                          int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
-                          int block_size, float scale, int dtype, const pkv_decode_options *opts,
-                          void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of pkv_paged_attn_decode and pkv_paged_attn_decode_append (new_k / new_v NULL: no append).
+int decode_impl(const void *q, const void *new_k, const void *new_v, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_lens, void *out,
+                float *lse, int num_seqs, int max_blocks_per_seq, int total_q, int max_q_len,
+                int max_context_len, int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
+                int block_size, float scale, int dtype, const pkv_decode_options *opts, void *workspace,
+                size_t workspace_bytes, void *stream) {
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                               head_dim, dtype, opts);
@@ -288,6 +293,12 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   // share boundaries must start ring cycles only where a partition end could fall inside a run
   a.cut_align = pl.num_parts > 1 ? pl.depth : 1;
   a.rows_per_tile = pl.rows_per_tile;
+  // the persistent matrix-core kernel appends in its own pass (up to 8 new tokens per sequence);
+  // every other launch appends with a small kernel first
+  const bool appending = new_k != nullptr;
+  const bool fused_append = appending && persist && pl.path == PKV_PATH_MFMA && max_q_len <= 8;
+  a.new_k = new_k;
+  a.new_v = new_v;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -310,6 +321,13 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
         hipSuccess)
       return PKV_ERR_LAUNCH;
   }
+  if (appending && !fused_append) {
+    if (pkv::launch_kv_append(a, bf16, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  if (!fused_append) {
+    a.new_k = nullptr;
+    a.new_v = nullptr;
+  }
   if (opts && opts->event_main_begin &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_begin), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
@@ -325,6 +343,37 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
     if (pkv::launch_combine(a, bf16, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          const int32_t *q_lens, void *out, float *lse, int num_seqs,
+                          int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
+                          int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
+                          int block_size, float scale, int dtype, const pkv_decode_options *opts,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                     num_seqs, max_blocks_per_seq, total_q, max_q_len, max_context_len, num_blocks, num_heads,
+                     num_kv_heads, head_dim, block_size, scale, dtype, opts, workspace, workspace_bytes,
+                     stream);
+}
+
+int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *new_v, void *k_cache,
+                                 void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *q_lens, void *out, float *lse, int num_seqs,
+                                 int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
+                                 int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, float scale, int dtype, const pkv_decode_options *opts,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_seqs > 0 && (!new_k || !new_v)) return PKV_ERR_NULL;
+  return decode_impl(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_seqs,
+                     max_blocks_per_seq, total_q, max_q_len, max_context_len, num_blocks, num_heads,
+                     num_kv_heads, head_dim, block_size, scale, dtype, opts, workspace, workspace_bytes,
+                     stream);
 }
 
 }  // extern "C"

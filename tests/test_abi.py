@@ -114,6 +114,17 @@ def test_workspace_and_partition_policy(lib):
     assert info.rows_per_tile == 32 and info.row_tiles == 1
 
 
+def test_append_argument_validation(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+
+    def call(nk, nv, S=4, D=64):
+        return lib.pkv_paged_attn_decode_append(fake, nk, nv, fake, fake, fake, fake, None, fake, None, S, 4, S,
+                                                1, 40, 16, 4, 2, D, 16, 0.125, 0, None, None, 0, None)
+    assert call(None, fake) == -1 and call(fake, None) == -1   # the new rows are required
+    assert call(fake, fake, D=96) == -3                        # then the decode's own checks
+    assert call(None, None, S=0) == 0                          # empty batch: no-op
+
+
 def test_probe_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
     assert lib.pkv_probe_page_stream(None, f, 8, 128, f, f, 4, f, None) == -1
