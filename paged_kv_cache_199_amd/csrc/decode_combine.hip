@@ -81,62 +81,96 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   };
   const int nsrc = si.nparts + ncand;
 
-  // the first 64 sources (usually all of them) are resolved once and kept for the second pass
-  float M = -INFINITY;
+  // whether the row needs a merge is arithmetic: decide it before any load of partials
   bool any_cut = false;
-  int64_t prow0 = base;   // a non-source lane points at partition 0's row (always written), weight 0
-  float lse0 = -INFINITY;
-  for (int c0 = 0; c0 < nsrc; c0 += 64) {
+  for (int c0 = si.nparts; c0 < nsrc && !any_cut; c0 += 64) {
     int64_t prow = base;
     bool cut = false;
-    const bool ok = c0 + lane < nsrc && source(c0 + lane, prow, cut);
-    any_cut |= cut;
-    const float l = ok ? a.part_lse[prow] : -INFINITY;
-    if (c0 == 0) {
-      prow0 = prow;
-      lse0 = l;
-    }
-    M = fmaxf(M, l);
+    if (c0 + lane < nsrc) source(c0 + lane, prow, cut);
+    any_cut = __builtin_amdgcn_ballot_w64(cut) != 0;
   }
   // a row whose item one wave covered in one piece already holds its final output
-  if (si.nparts <= 1 && __builtin_amdgcn_ballot_w64(any_cut) == 0) return;
-  M = wave_max(M);
-  const float Ms = M == -INFINITY ? 0.f : M;
+  if (si.nparts <= 1 && !any_cut) return;
 
   float acc[DPL];
   #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
   float L2 = 0.f;
-  for (int c0 = 0; c0 < nsrc; c0 += 64) {
-    int64_t prow = prow0;
-    float l = lse0;
-    if (c0 > 0) {
-      bool cut = false;
-      prow = base;
-      l = c0 + lane < nsrc && source(c0 + lane, prow, cut) ? a.part_lse[prow] : -INFINITY;
-    }
-    const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
-    L2 += wl;
+  float Ms = 0.f;
+  if (nsrc <= 16) {
+    // the usual case: the LSEs and the partial rows of all sources are loaded together (the rows do
+    // not depend on the weights), so the merge waits for memory once
+    int64_t prow = base;   // a non-source lane points at partition 0's row (always written), weight 0
+    bool cut = false;
+    const bool ok = lane < nsrc && source(lane, prow, cut);
+    const float l = ok ? a.part_lse[prow] : -INFINITY;
     const int lo = (int)prow;
     const int hi = (int)(prow >> 32);
-    const int n = min(64, nsrc - c0);
-    // batches of 16 sources, all loads of a batch in flight together; a lane past the chunk's end
-    // reads partition 0's row with weight 0
-    for (int j = 0; j < n; j += 16) {
-      float v[16][DPL];
+    float v[16][DPL];
+    #pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t pr = u < nsrc ? ((int64_t)__shfl(hi, u) << 32) | (uint32_t)__shfl(lo, u) : base;
+      const float *op = a.part_o + pr * D + lane;
       #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int src = min(j + u, 63);
-        const int64_t pr = j + u < n ? ((int64_t)__shfl(hi, src) << 32) | (uint32_t)__shfl(lo, src) : base;
-        const float *op = a.part_o + pr * D + lane;
-        #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[u][k] = op[64 * k];
+      for (int k = 0; k < DPL; ++k) v[u][k] = op[64 * k];
+    }
+    const float M = wave_max(l);
+    Ms = M == -INFINITY ? 0.f : M;
+    const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
+    L2 = wl;
+    #pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float wp = u < nsrc ? __shfl(wl, u) : 0.f;
+      #pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, v[u][k], acc[k]);
+    }
+  } else {
+    // many sources: max over all LSEs first, then the weighted rows in batches of 16
+    float M = -INFINITY;
+    int64_t prow0 = base;
+    float lse0 = -INFINITY;
+    for (int c0 = 0; c0 < nsrc; c0 += 64) {
+      int64_t prow = base;
+      bool cut = false;
+      const bool ok = c0 + lane < nsrc && source(c0 + lane, prow, cut);
+      const float l = ok ? a.part_lse[prow] : -INFINITY;
+      if (c0 == 0) {
+        prow0 = prow;
+        lse0 = l;
       }
-      #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float wp = j + u < n ? __shfl(wl, min(j + u, 63)) : 0.f;
+      M = fmaxf(M, l);
+    }
+    M = wave_max(M);
+    Ms = M == -INFINITY ? 0.f : M;
+    for (int c0 = 0; c0 < nsrc; c0 += 64) {
+      int64_t prow = prow0;
+      float l = lse0;
+      if (c0 > 0) {
+        bool cut = false;
+        prow = base;
+        l = c0 + lane < nsrc && source(c0 + lane, prow, cut) ? a.part_lse[prow] : -INFINITY;
+      }
+      const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
+      L2 += wl;
+      const int lo = (int)prow;
+      const int hi = (int)(prow >> 32);
+      const int n = min(64, nsrc - c0);
+      for (int j = 0; j < n; j += 16) {
+        float v[16][DPL];
         #pragma unroll
-        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, v[u][k], acc[k]);
+        for (int u = 0; u < 16; ++u) {
+          const int src = min(j + u, 63);
+          const int64_t pr = j + u < n ? ((int64_t)__shfl(hi, src) << 32) | (uint32_t)__shfl(lo, src) : base;
+          const float *op = a.part_o + pr * D + lane;
+          #pragma unroll
+          for (int k = 0; k < DPL; ++k) v[u][k] = op[64 * k];
+        }
+        #pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float wp = j + u < n ? __shfl(wl, min(j + u, 63)) : 0.f;
+          #pragma unroll
+          for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wp, v[u][k], acc[k]);
+        }
       }
     }
   }
