@@ -35,6 +35,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 def algorithmic_bytes(w) -> int:
     """Bytes the decode must move at least once (split-K partials excluded: they are overhead)."""
     e = 4 if w.spec.dtype == "f32" else 2
+    ekv = 1 if w.kv_fp8 else e                       # E4M3 pools: one byte per element
     KVH, D, B = w.spec.num_kv_heads, w.spec.head_dim, w.spec.block_size
     rows_by_block = {}
     for s in range(w.num_seqs):
@@ -43,7 +44,7 @@ def algorithmic_bytes(w) -> int:
             blk = int(w.block_tables[s, j])
             rows_by_block[blk] = max(rows_by_block.get(blk, 0), min(B, n - j * B))
     kv_tokens = sum(rows_by_block.values())          # shared pages count once
-    kv = kv_tokens * KVH * D * 2 * e
+    kv = kv_tokens * KVH * D * 2 * ekv
     qo = w.total_q * w.spec.num_heads * D * e * 2 + w.total_q * w.spec.num_heads * 4
     meta = int(((w.context_lens.astype(np.int64) + B - 1) // B).sum()) * 4 + w.num_seqs * 8
     return int(kv + qo + meta)
@@ -53,8 +54,9 @@ def write_bytes(w) -> int:
     if w.slot_mapping is None:
         return 0
     e = 4 if w.spec.dtype == "f32" else 2
+    ekv = 1 if w.kv_fp8 else e
     rows = int(w.slot_mapping.shape[0])
-    return rows * w.spec.num_kv_heads * w.spec.head_dim * e * 2 * 2 + rows * 8
+    return rows * w.spec.num_kv_heads * w.spec.head_dim * (e + ekv) * 2 + rows * 8
 
 
 def kernel_source_hash() -> str:
@@ -162,20 +164,33 @@ def cpu_baseline(w, budget_s: float):
         t = t.detach().cpu().contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
+    from oracle import fp8 as F8
+
     q, kc, vc = bits(w.q), bits(w.k_cache), bits(w.v_cache)
     B = w.spec.block_size
     e = 4 if w.spec.dtype == "f32" else 2
+    ekv = 1 if w.kv_fp8 else e
     t_used, nbytes, tokens, n_runs = 0.0, 0, 0, 0
     with threadpool_limits(limits=1):
         while t_used < budget_s:
             s = n_runs % w.num_seqs
-            t0 = time.perf_counter()
-            O.paged_decode_attention(q, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale,
-                                     w.spec.num_kv_heads, B, seqs=[s])
-            t_used += time.perf_counter() - t0
             n = int(w.context_lens[s])
+            t0 = time.perf_counter()
+            if w.kv_fp8:
+                # E4M3 pools: decode the sequence's pages (part of the oracle's work), then attend
+                ids = w.block_tables[s, :(n + B - 1) // B].astype(np.int64)
+                kd = F8.dequantize(kc[ids], w.spec.k_scale)
+                vd = F8.dequantize(vc[ids], w.spec.v_scale)
+                table = np.full_like(w.block_tables, -1)
+                table[s, :ids.shape[0]] = np.arange(ids.shape[0])
+                O.paged_decode_attention(q, kd, vd, table, w.context_lens, w.q_lens, w.scale, w.spec.num_kv_heads,
+                                         B, seqs=[s])
+            else:
+                O.paged_decode_attention(q, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale,
+                                         w.spec.num_kv_heads, B, seqs=[s])
+            t_used += time.perf_counter() - t0
             qs = int(w.q_lens[s])
-            nbytes += n * w.spec.num_kv_heads * w.spec.head_dim * 2 * e + qs * w.spec.num_heads * (
+            nbytes += n * w.spec.num_kv_heads * w.spec.head_dim * 2 * ekv + qs * w.spec.num_heads * (
                 w.spec.head_dim * e * 2 + 4) + ((n + B - 1) // B) * 4 + 8
             tokens += n
             n_runs += 1
@@ -248,7 +263,7 @@ def main():
     vcs = [w.v_cache] + [w.v_cache.clone() for _ in range(R - 1)]
     out = torch.empty_like(w.q)
     lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
-    code = _lib.PKV_BF16 if spec.dtype == "bf16" else _lib.PKV_F32
+    code = (_lib.PKV_BF16_FP8KV if spec.kv_fp8 else _lib.PKV_BF16) if spec.dtype == "bf16" else _lib.PKV_F32
     sched = {"auto": 0, "grid": 1, "persistent": 2}[args.schedule]
     plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, P, path,
                             args.depth, sched, args.wgs_per_cu)
@@ -280,12 +295,15 @@ def main():
 
     ev = [(new_event(), new_event()) for _ in range(args.steps)]
 
+    # E4M3 pools append through the quantizing slot-mapped write (the fused append is bf16 only)
+    append_mode = "slots" if spec.kv_fp8 else args.append
     dstep = _lib.DecodeStep(w.q, kcs[0], vcs[0], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
                             H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
                             partition_size=P, path=path, depth=args.depth, schedule=sched, workspace=ws,
                             new_k=w.new_k, new_v=w.new_v,
-                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None and args.append == "slots"
-                            else None, wgs_per_cu=args.wgs_per_cu)
+                            slot_mapping=meta["slot_mapping"] if w.slot_mapping is not None and append_mode == "slots"
+                            else None, wgs_per_cu=args.wgs_per_cu,
+                            k_scale=spec.k_scale if spec.kv_fp8 else 0.0, v_scale=spec.v_scale if spec.kv_fp8 else 0.0)
 
     def step(i, events=None):
         r = i % R
@@ -369,7 +387,8 @@ def main():
             "path": kernel.split("_")[1], "schedule": sched_name,
             "pipeline_depth": plan["pipeline_depth"], "grid_waves": plan["grid_waves"], "pool_copies": R,
             "appends_new_token": w.slot_mapping is not None,
-            "append": (args.append if w.slot_mapping is not None else None),
+            "append": (append_mode if w.slot_mapping is not None else None),
+            "kv_cache": "e4m3" if spec.kv_fp8 else spec.dtype,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

@@ -29,7 +29,8 @@
  *     slot_mapping   int64 [num_tokens]  slot = physical_block * block_size + offset; < 0 skips the row
  * Logical token t of sequence s sits in block block_tables[s][t / block_size] at offset t % block_size.
  *
- * Element types: PKV_F32 (q, caches, out all fp32) or PKV_BF16 (all bf16).  head_dim is 64 or 128,
+ * Element types: PKV_F32 (q, caches, out all fp32), PKV_BF16 (all bf16) or PKV_BF16_FP8KV (bf16 q
+ * and out, E4M3 pools; see below).  head_dim is 64 or 128,
  * block_size is 16.
  *
  * Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream).  They never allocate,
@@ -59,7 +60,13 @@ typedef enum pkv_status {
   PKV_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
 } pkv_status;
 
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+/* PKV_BF16_FP8KV: q, out and appended rows bf16; the K and V pools hold 8-bit E4M3 codes (sign, 4-bit
+ * exponent with bias 7, 3-bit mantissa, no infinities, one NaN pattern per sign, largest finite
+ * value 448) standing for code * k_scale and code * v_scale (pkv_decode_options; the scales of the
+ * pools, 0 meaning 1).  Half the cache bytes of bf16 (lfm25-inference, "Current Scope and
+ * Limitations": FP8 KV storage is the step after its BF16 KV cache).  Decode only on the
+ * matrix-core persistent schedule. */
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1, PKV_BF16_FP8KV = 2 } pkv_dtype;
 
 /* Kernel family for the partition pass.  AUTO lets the library choose. */
 typedef enum pkv_path { PKV_PATH_AUTO = 0, PKV_PATH_VALU = 1, PKV_PATH_MFMA = 2 } pkv_path;
@@ -88,6 +95,8 @@ typedef struct pkv_decode_options {
   void *event_main_end;     /* hipEvent_t recorded right after it (before the combine kernel) */
   int workgroups_per_cu;    /* persistent schedule: resident workgroups per CU, at most what fits
                                (0 = policy) */
+  float k_scale;            /* PKV_BF16_FP8KV: the K pool's scale (0 = 1); ignored otherwise */
+  float v_scale;            /* PKV_BF16_FP8KV: the V pool's scale (0 = 1); ignored otherwise */
 } pkv_decode_options;
 
 /*
@@ -105,6 +114,19 @@ int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping
                        int64_t num_tokens, int64_t num_blocks,
                        int num_kv_heads, int head_dim, int block_size,
                        int dtype, void *stream);
+
+/*
+ * Slot-mapped append into E4M3 pools (PKV_BF16_FP8KV): as pkv_kv_cache_write, but k / v are bf16 and
+ * each element is stored as the E4M3 code nearest to x / scale (x widened to fp32, the division
+ * correctly rounded in fp32), ties to the even code, magnitudes beyond 448 saturating to 448, NaN to
+ * the NaN code of its sign.  k_scale / v_scale > 0.  k_cache [num_blocks, KVH, block_size, head_dim]
+ * and v_cache [num_blocks, KVH, head_dim, block_size] of uint8 codes.
+ */
+int pkv_kv_cache_write_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                           void *k_cache, void *v_cache,
+                           int64_t num_tokens, int64_t num_blocks,
+                           int num_kv_heads, int head_dim, int block_size,
+                           float k_scale, float v_scale, void *stream);
 
 /*
  * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options (0 is possible:

@@ -15,7 +15,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_BF16_FP8KV = 0, 1, 2
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_GRID, SCHEDULE_PERSISTENT = 0, 1, 2
 BLOCK_SIZE = 16
@@ -26,7 +26,7 @@ _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 class DecodeOptions(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("path", _c_int), ("pipeline_depth", _c_int),
                 ("schedule", _c_int), ("event_main_begin", _vp), ("event_main_end", _vp),
-                ("workgroups_per_cu", _c_int)]
+                ("workgroups_per_cu", _c_int), ("k_scale", _c_f), ("v_scale", _c_f)]
 
 
 class DecodePlanInfo(ctypes.Structure):
@@ -49,6 +49,8 @@ EXPORTS = {
                                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                               _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                               ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
+    "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
+                                        _vp]),
     "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_version": (_c_int, []),
@@ -85,6 +87,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _decode_code(q, k_cache, v_cache, out) -> int:
+    """dtype code of a decode call: all fp32, all bf16, or bf16 q/out over uint8 E4M3 pools."""
+    for t in (q, k_cache, v_cache, out):
+        _need(t.is_contiguous() and t.is_cuda, "q, caches and out: contiguous, on the GPU")
+    _need(out.dtype == q.dtype and k_cache.dtype == v_cache.dtype, "out matches q, V pool matches K pool")
+    if q.dtype == torch.bfloat16 and k_cache.dtype == torch.uint8:
+        return PKV_BF16_FP8KV
+    _need(k_cache.dtype == q.dtype, "caches in q's dtype (or uint8 E4M3 codes with bf16 q)")
+    return _dtype_code(q)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -100,8 +113,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _opts(partition_size: int, path: int, events, depth: int = 0, schedule: int = 0,
-          wgs_per_cu: int = 0) -> DecodeOptions:
-    o = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
+          wgs_per_cu: int = 0, k_scale: float = 0.0, v_scale: float = 0.0) -> DecodeOptions:
+    o = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu, k_scale, v_scale)
     if events is not None:
         b, e = events
         o.event_main_begin = b.cuda_event
@@ -126,6 +139,25 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     rc = lib.pkv_kv_cache_write(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
                                 T, NB, KVH, D, BLOCK_SIZE, _dtype_code(k), _stream(stream))
     _check(rc, "pkv_kv_cache_write")
+
+
+def kv_cache_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, k_scale: float, v_scale: float, stream=None) -> None:
+    """bf16 k/v [T, KVH, D] -> E4M3 codes in uint8 pools k_cache [NB, KVH, 16, D] / v_cache [NB, KVH, D, 16]."""
+    lib = load()
+    _need(k.dim() == 3 and k.shape == v.shape and k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16,
+          "k and v: bf16 [T, KVH, D] of one shape")
+    T, KVH, D = k.shape
+    NB = k_cache.shape[0]
+    _need(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8, "uint8 code pools")
+    _need(tuple(k_cache.shape) == (NB, KVH, BLOCK_SIZE, D) and tuple(v_cache.shape) == (NB, KVH, D, BLOCK_SIZE),
+          "k_cache [NB, KVH, 16, D], v_cache [NB, KVH, D, 16]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T, "slot_mapping: int64 [T]")
+    for t in (k, v, k_cache, v_cache, slot_mapping):
+        _need(t.is_contiguous() and t.is_cuda, "contiguous, on the GPU")
+    rc = lib.pkv_kv_cache_write_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), T, NB, KVH,
+                                    D, BLOCK_SIZE, float(k_scale), float(v_scale), _stream(stream))
+    _check(rc, "pkv_kv_cache_write_fp8")
 
 
 def decode_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
@@ -172,7 +204,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       path: int = PATH_AUTO, workspace: Optional[torch.Tensor] = None,
                       events=None, stream=None, depth: int = 0, schedule: int = 0,
                       wgs_per_cu: int = 0, new_k: Optional[torch.Tensor] = None,
-                      new_v: Optional[torch.Tensor] = None) -> None:
+                      new_v: Optional[torch.Tensor] = None, k_scale: float = 0.0, v_scale: float = 0.0) -> None:
     """Decode attention through the C ABI.  q/out [total_q, H, D]; lse fp32 [total_q, H] or None.
 
     With new_k / new_v ([total_q, KVH, D], packed like q) the step appends them first, at each
@@ -191,8 +223,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
     _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    for t in (q, k_cache, v_cache, out):
-        _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "same dtype, contiguous, on the GPU")
+    code = _decode_code(q, k_cache, v_cache, out)
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
           and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
     _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
@@ -201,8 +232,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     if lse is not None:
         _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
               "lse: fp32 [total_q, H]")
-    code = _dtype_code(q)
-    o = _opts(partition_size, path, events, depth, schedule, wgs_per_cu)
+    o = _opts(partition_size, path, events, depth, schedule, wgs_per_cu, k_scale, v_scale)
     need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                               num_kv_heads, head_dim, code, ctypes.byref(o)))
     if workspace is None and need > 0:
@@ -240,7 +270,7 @@ class DecodeStep:
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
                  num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len=1,
                  partition_size=0, path=PATH_AUTO, depth=0, schedule=0, workspace=None,
-                 new_k=None, new_v=None, slot_mapping=None, wgs_per_cu=0):
+                 new_k=None, new_v=None, slot_mapping=None, wgs_per_cu=0, k_scale=0.0, v_scale=0.0):
         lib = load()
         self._lib = lib
         total_q = q.shape[0]
@@ -251,8 +281,7 @@ class DecodeStep:
         _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
         _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-        for t in (q, k_cache, v_cache, out):
-            _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "same dtype, contiguous, on the GPU")
+        code = _decode_code(q, k_cache, v_cache, out)
         _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
               and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
         _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
@@ -262,9 +291,9 @@ class DecodeStep:
         if lse is not None:
             _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads)
                   and lse.is_contiguous(), "lse: fp32 [total_q, H]")
-        code = _dtype_code(q)
-        self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
-        self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu)
+        self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu, k_scale, v_scale)
+        self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu, k_scale,
+                                      v_scale)
         need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                                   num_kv_heads, head_dim, code, ctypes.byref(self._opts)))
         if workspace is None and need > 0:
@@ -295,8 +324,14 @@ class DecodeStep:
                   and slot_mapping.is_cuda, "slot_mapping: int64 [T] on the GPU")
             for t in (new_k, new_v):
                 _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, on the GPU")
-            self._write = ((_ptr(new_k), _ptr(new_v), _ptr(slot_mapping)),
-                           (T, NB, num_kv_heads, head_dim, block_size, code))
+            if code == PKV_BF16_FP8KV:
+                _need(k_scale > 0 and v_scale > 0, "E4M3 pools need k_scale / v_scale > 0 for the write")
+                self._write = ((_ptr(new_k), _ptr(new_v), _ptr(slot_mapping)),
+                               (T, NB, num_kv_heads, head_dim, block_size, float(k_scale), float(v_scale)))
+            else:
+                self._write = ((_ptr(new_k), _ptr(new_v), _ptr(slot_mapping)),
+                               (T, NB, num_kv_heads, head_dim, block_size, code))
+            self._write_fp8 = code == PKV_BF16_FP8KV
         self._kc, self._vc = _ptr(k_cache), _ptr(v_cache)
 
     def __call__(self, k_cache=None, v_cache=None, events=None, stream=None):
@@ -306,7 +341,10 @@ class DecodeStep:
         lib = self._lib
         if self._write is not None:
             ptrs, sizes = self._write
-            rc = lib.pkv_kv_cache_write(*ptrs, kc, vc, *sizes, st)
+            if self._write_fp8:
+                rc = lib.pkv_kv_cache_write_fp8(*ptrs, kc, vc, *sizes, st)
+            else:
+                rc = lib.pkv_kv_cache_write(*ptrs, kc, vc, *sizes, st)
             if rc != 0:
                 _check(rc, "pkv_kv_cache_write")
         o = self._opts

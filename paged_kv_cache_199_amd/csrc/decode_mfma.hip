@@ -131,7 +131,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // LDS tables of the persistent schedule, per sequence s: pre = stream pages of sequences < s (for
 // one kv head), ctx = clamped context length, qb = first q row, rts = row tiles, qs = clamped new
 // tokens.  Workgroup 0 also leaves pre in the workspace for the combine kernel.
-template <int D, int NT, int NBUF, bool APPEND>
+template <int D, int NT, int NBUF, bool APPEND, bool F8>
 __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs a) {
   constexpr int ROWS = 16 * NT;
   constexpr int APP = 2 * AppendRows<D>::MAXQ * AppendRows<D>::CH;   // staging chunks per wave
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
     WaveAcc<D, NT> st;
     init_acc<D, NT>(st);
-    stream_pages<D, NT, NBUF>(
+    stream_pages<D, NT, NBUF, F8>(
         a, si, kvh, bt_row, j0, j0 + run, PP, lane, w, st,
         [&](int part, int first, int end) {
           const bool whole = first == 0 && end == nblk && si.nparts == 1;
@@ -272,21 +272,22 @@ int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent) { retur
 int persistent_max_seqs() { return 4096; }
 size_t persistent_lds_bytes(int num_seqs) { return (size_t)(5 * num_seqs + 1) * sizeof(int); }
 
+template <int D, int NT, bool APPEND, bool F8>
+static void launch_persistent(const DecodeArgs &a, int depth, int grid, hipStream_t st) {
+  const size_t lds = persistent_lds_bytes(a.num_seqs);
+  if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2, APPEND, F8><<<grid, 256, lds, st>>>(a);
+  else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3, APPEND, F8><<<grid, 256, lds, st>>>(a);
+  else decode_mfma_persistent_kernel<D, NT, 4, APPEND, F8><<<grid, 256, lds, st>>>(a);
+}
+
+// f8: E4M3 pools (persistent schedule only, no fused append).
 template <int D, int NT>
-static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent, int grid,
+static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent, int grid, bool f8,
                                  hipStream_t st) {
   if (persistent) {
-    const int g = grid;
-    const size_t lds = persistent_lds_bytes(a.num_seqs);
-    if (a.new_k) {
-      if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2, true><<<g, 256, lds, st>>>(a);
-      else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3, true><<<g, 256, lds, st>>>(a);
-      else decode_mfma_persistent_kernel<D, NT, 4, true><<<g, 256, lds, st>>>(a);
-    } else {
-      if (depth == 2) decode_mfma_persistent_kernel<D, NT, 2, false><<<g, 256, lds, st>>>(a);
-      else if (depth == 3) decode_mfma_persistent_kernel<D, NT, 3, false><<<g, 256, lds, st>>>(a);
-      else decode_mfma_persistent_kernel<D, NT, 4, false><<<g, 256, lds, st>>>(a);
-    }
+    if (f8) launch_persistent<D, NT, false, true>(a, depth, grid, st);
+    else if (a.new_k) launch_persistent<D, NT, true, false>(a, depth, grid, st);
+    else launch_persistent<D, NT, false, false>(a, depth, grid, st);
     return hipGetLastError();
   }
   switch (depth) {
@@ -301,7 +302,7 @@ static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent
 template <int D, int NT, int NBUF>
 static int occupancy_of(int num_seqs) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_persistent_kernel<D, NT, NBUF, false>, 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_persistent_kernel<D, NT, NBUF, false, false>, 256,
                                                    persistent_lds_bytes(num_seqs)) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -331,13 +332,13 @@ int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int n
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, int depth,
-                              bool persistent, int grid, hipStream_t st) {
+                              bool persistent, int grid, bool f8, hipStream_t st) {
   if (head_dim == 64) {
-    return rows_per_tile > 16 ? launch_mfma_dn<64, 2>(a, depth, persistent, grid, st)
-                              : launch_mfma_dn<64, 1>(a, depth, persistent, grid, st);
+    return rows_per_tile > 16 ? launch_mfma_dn<64, 2>(a, depth, persistent, grid, f8, st)
+                              : launch_mfma_dn<64, 1>(a, depth, persistent, grid, f8, st);
   }
-  return rows_per_tile > 16 ? launch_mfma_dn<128, 2>(a, depth, persistent, grid, st)
-                            : launch_mfma_dn<128, 1>(a, depth, persistent, grid, st);
+  return rows_per_tile > 16 ? launch_mfma_dn<128, 2>(a, depth, persistent, grid, f8, st)
+                            : launch_mfma_dn<128, 1>(a, depth, persistent, grid, f8, st);
 }
 
 }  // namespace pkv

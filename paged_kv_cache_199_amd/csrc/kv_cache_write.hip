@@ -90,6 +90,73 @@ hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStr
   return hipGetLastError();
 }
 
+// The E4M3 code of x: the nearest code, ties to the even code, magnitudes from 448 up saturating to
+// 448 (code 0x7E), NaN to the NaN code of its sign.  Below 2^-6 the codes are the multiples of 2^-9
+// (code = multiple; 8 is the smallest normal, so the two ranges join); above, the code keeps the
+// three leading fraction bits of x rounded half to even, with a carry into the exponent.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return sign | 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.f);
+  const uint32_t ab = __float_as_uint(a);
+  int e = (int)(ab >> 23) - 127;                       // -6 .. 8
+  uint32_t m = (ab >> 20) & 7u;
+  const uint32_t rest = ab & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
+  if (m == 8u) {
+    m = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | m;
+}
+
+// Slot-mapped append into E4M3 pools: bf16 rows in, one code per element out (x / scale in fp32).
+template <int D>
+__global__ __launch_bounds__(64) void kv_write_fp8_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                                          const int64_t *__restrict__ slots, uint8_t *__restrict__ kc,
+                                                          uint8_t *__restrict__ vc, int64_t num_slots, int kvh_n,
+                                                          float k_scale, float v_scale) {
+  constexpr int PER = D / 64;
+  const int64_t row = blockIdx.x;            // token * kvh_n + head
+  const int64_t t = row / kvh_n;
+  const int h = (int)(row - t * kvh_n);
+  const int lane = threadIdx.x;
+  const int64_t slot = slots[t];
+  uint32_t kq[PER], vq[PER];
+  #pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane + 64 * e;
+    kq[e] = e4m3_code(__uint_as_float((uint32_t)k[row * D + d] << 16) / k_scale);
+    vq[e] = e4m3_code(__uint_as_float((uint32_t)v[row * D + d] << 16) / v_scale);
+  }
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot - blk * kBlock);
+  const int64_t page = blk * kvh_n + h;
+  #pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane + 64 * e;
+    kc[(page * kBlock + off) * D + d] = (uint8_t)kq[e];
+    vc[(page * D + d) * kBlock + off] = (uint8_t)vq[e];
+  }
+}
+
+hipError_t launch_kv_write_fp8(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,
+                               int64_t num_tokens, int64_t num_blocks, int kvh_n, int head_dim, float k_scale,
+                               float v_scale, hipStream_t st) {
+  const int64_t grid = num_tokens * kvh_n;
+  const int64_t nslots = num_blocks * kBlock;
+  const uint16_t *ks = static_cast<const uint16_t *>(k);
+  const uint16_t *vs = static_cast<const uint16_t *>(v);
+  uint8_t *kd = static_cast<uint8_t *>(kc);
+  uint8_t *vd = static_cast<uint8_t *>(vc);
+  if (head_dim == 64) kv_write_fp8_kernel<64><<<grid, 64, 0, st>>>(ks, vs, slots, kd, vd, nslots, kvh_n, k_scale, v_scale);
+  else kv_write_fp8_kernel<128><<<grid, 64, 0, st>>>(ks, vs, slots, kd, vd, nslots, kvh_n, k_scale, v_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_write(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,
                            int64_t num_tokens, int64_t num_blocks, int kvh_n, int head_dim, bool bf16,
                            hipStream_t st) {

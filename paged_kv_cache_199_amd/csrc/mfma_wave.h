@@ -222,14 +222,57 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 // (the block table is read-only here): the id of the page issued NBUF steps later is fetched while
 // the current page is computed, so those loads never hold up the vector loads and a run of any
 // length streams without a restart.
-template <int D, int NT, int NBUF, class Flush, class Patch>
+// Two E4M3 codes (the low or high half of w) to two bf16 in one word, exactly: every E4M3 value is a
+// bf16 value, so the hardware's exact fp8 -> f32 conversion followed by dropping the low 16 bits
+// loses nothing.
+typedef float float2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// Registers of one page for one lane as loaded (bf16: already the MFMA operand layout; E4M3: half the
+// bytes, widened to it just before use).
+template <bool F8> struct KvRaw {
+  typedef uint4 K;      // 8 bf16 of one token row: the score product's A operand
+  typedef uint2 V;      // 4 tokens of one dim: the value product's A operand
+};
+template <> struct KvRaw<true> {
+  typedef uint2 K;      // 8 E4M3 codes
+  typedef uint32_t V;   // 4 E4M3 codes
+};
+
+template <int D>
+__device__ __forceinline__ void widen_page(const uint4 *kin, const uint2 *vin, uint4 *kout, uint2 *vout) {
+  #pragma unroll
+  for (int c = 0; c < D / 32; ++c) kout[c] = kin[c];
+  #pragma unroll
+  for (int t = 0; t < D / 16; ++t) vout[t] = vin[t];
+}
+template <int D>
+__device__ __forceinline__ void widen_page(const uint2 *kin, const uint32_t *vin, uint4 *kout, uint2 *vout) {
+  #pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    kout[c] = make_uint4(fp8x2_to_bf16x2<false>(kin[c].x), fp8x2_to_bf16x2<true>(kin[c].x),
+                         fp8x2_to_bf16x2<false>(kin[c].y), fp8x2_to_bf16x2<true>(kin[c].y));
+  #pragma unroll
+  for (int t = 0; t < D / 16; ++t) vout[t] = make_uint2(fp8x2_to_bf16x2<false>(vin[t]), fp8x2_to_bf16x2<true>(vin[t]));
+}
+
+// F8: the pools hold E4M3 codes (1 byte per element) instead of bf16; pages are half as large and are
+// widened in registers right before their products.
+template <int D, int NT, int NBUF, bool F8, class Flush, class Patch>
 __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
                                              const int32_t *bt_row, int jb, int je, int PP, int lane,
                                              const WaveRows<D, NT> &w, WaveAcc<D, NT> &st,
                                              Flush flush, Patch patch) {
-  constexpr int ROWB = D * 2;
+  constexpr int EB = F8 ? 1 : 2;          // bytes per cache element
+  constexpr int ROWB = D * EB;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
+  typedef typename KvRaw<F8>::K KR;
+  typedef typename KvRaw<F8>::V VR;
   const int n = je - jb;
   if (n <= 0) return;
   const int col = lane & 15;
@@ -243,18 +286,26 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   const int last = je - 1;
   auto id_of = [&](int j) -> int { return btc[__builtin_amdgcn_readfirstlane(min(j, last))]; };
 
-  uint4 kb[NBUF][NK];
-  uint2 vb[NBUF][ND];
+  KR kb[NBUF][NK];
+  VR vb[NBUF][ND];
   bool okb[NBUF];
-  auto issue = [&](int bid, uint4 *kr, uint2 *vr, bool &ok) {
+  auto issue = [&](int bid, KR *kr, VR *vr, bool &ok) {
     ok = bid >= 0 && bid < nb;
     const int64_t off = ((int64_t)(ok ? bid : 0) * KVH + kvh) * page_bytes;
-    const char *kp = kbase + off + col * ROWB + grp * 16;
+    const char *kp = kbase + off + col * ROWB + grp * 8 * EB;
     #pragma unroll
-    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
-    const char *vp = vbase + off + (col * kBlock + 4 * grp) * 2;
+    for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const KR *>(kp + c * 32 * EB);
+    const char *vp = vbase + off + (col * kBlock + 4 * grp) * EB;
     #pragma unroll
-    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
+    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
+  };
+  // widen (E4M3) or take (bf16) page b of the ring, then substitute appended tokens, then compute
+  auto compute = [&](int j, const KR *kr, const VR *vr, bool ok) {
+    uint4 kc[NK];
+    uint2 vc[ND];
+    widen_page<D>(kr, vr, kc, vc);
+    patch(j, kc, vc);
+    mfma_page<D, NT>(a, si, j * kBlock, kc, vc, ok, lane, w, st);
   };
 
   int sid[NBUF];
@@ -270,8 +321,7 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
       const int bn = (b + NBUF - 1) % NBUF;   // constants once the loop is unrolled
       issue(sid[b], kb[bn], vb[bn], okb[bn]);
       sid[b] = id_of(jb + j0 + b + 2 * NBUF - 1);
-      patch(jb + j0 + b, kb[b], vb[b]);
-      mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
+      compute(jb + j0 + b, kb[b], vb[b], okb[b]);
     }
     const int jl = jb + j0 + NBUF - 1;
     if ((jl + 1) % PP == 0 || jl == last) {
@@ -282,10 +332,7 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   if (j0 < n) {
     #pragma unroll
     for (int b = 0; b < NBUF - 1; ++b) {
-      if (j0 + b < n) {
-        patch(jb + j0 + b, kb[b], vb[b]);
-        mfma_page<D, NT>(a, si, (jb + j0 + b) * kBlock, kb[b], vb[b], okb[b], lane, w, st);
-      }
+      if (j0 + b < n) compute(jb + j0 + b, kb[b], vb[b], okb[b]);
     }
     flush(last / PP, piece, je);
   }
@@ -426,7 +473,7 @@ __device__ __forceinline__ void finish_wave(const DecodeArgs &a, int p, bool sin
     l += __shfl_xor(l, 32);
     if (w.last[n] < 0) continue;
     const bool seen = l > 0.f;
-    const float inv = seen ? 1.f / l : 0.f;
+    const float inv = seen ? a.v_scale / l : 0.f;   // v_scale: the V pool's scale (1 for bf16 pools)
     const float lse2 = seen ? st.m[n] + log2_hw(l) : -INFINITY;
     const int64_t orow = w.orow[n];
     if (single) {

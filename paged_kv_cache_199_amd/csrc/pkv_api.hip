@@ -15,7 +15,10 @@ hipError_t launch_decode_valu(const DecodeArgs &a, bool bf16, int head_dim, int 
                               hipStream_t st);
 int valu_max_rows(bool bf16);
 hipError_t launch_decode_mfma(const DecodeArgs &a, int head_dim, int rows_per_tile, int depth,
-                              bool persistent, int grid, hipStream_t st);
+                              bool persistent, int grid, bool f8, hipStream_t st);
+hipError_t launch_kv_write_fp8(const void *k, const void *v, const int64_t *slots, void *kc, void *vc,
+                               int64_t num_tokens, int64_t num_blocks, int kvh_n, int head_dim, float k_scale,
+                               float v_scale, hipStream_t st);
 int mfma_rows_per_tile(int rows);
 int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent);
 int persistent_max_seqs();
@@ -49,7 +52,8 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-bool supported_dtype(int dtype) { return dtype == PKV_F32 || dtype == PKV_BF16; }
+bool supported_dtype(int dtype) { return dtype == PKV_F32 || dtype == PKV_BF16 || dtype == PKV_BF16_FP8KV; }
+bool valid_scale(float s) { return s == 0.f || (s > 0.f && s < 3.0e38f); }
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 struct Plan {
@@ -78,7 +82,10 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
     if (P < 0 || P % kBlockSize != 0) return PKV_ERR_UNSUPPORTED;
     if (opts->path != PKV_PATH_AUTO && opts->path != PKV_PATH_VALU && opts->path != PKV_PATH_MFMA)
       return PKV_ERR_UNSUPPORTED;
-    if (opts->path == PKV_PATH_MFMA && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (opts->path == PKV_PATH_MFMA && dtype == PKV_F32) return PKV_ERR_UNSUPPORTED;
+    if (dtype == PKV_BF16_FP8KV && (opts->path == PKV_PATH_VALU || opts->schedule == PKV_SCHEDULE_GRID))
+      return PKV_ERR_UNSUPPORTED;
+    if (!valid_scale(opts->k_scale) || !valid_scale(opts->v_scale)) return PKV_ERR_UNSUPPORTED;
     if (opts->pipeline_depth != 0 && (opts->pipeline_depth < 2 || opts->pipeline_depth > 4))
       return PKV_ERR_UNSUPPORTED;
     if (opts->schedule < 0 || opts->schedule > PKV_SCHEDULE_PERSISTENT) return PKV_ERR_UNSUPPORTED;
@@ -99,7 +106,7 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
                int num_kv_heads, int head_dim, int dtype, bool ragged_q,
                const pkv_decode_options *opts) {
   Plan pl{};
-  const bool bf16 = dtype == PKV_BF16;
+  const bool bf16 = dtype != PKV_F32;
   const int G = num_heads / num_kv_heads;
   const int rows = G * max_q_len;
   const int asked = opts ? opts->path : PKV_PATH_AUTO;
@@ -199,7 +206,7 @@ const char *pkv_status_string(int status) {
 int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
                        void *v_cache, int64_t num_tokens, int64_t num_blocks, int num_kv_heads,
                        int head_dim, int block_size, int dtype, void *stream) {
-  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || block_size != kBlockSize)
+  if ((dtype != PKV_F32 && dtype != PKV_BF16) || !supported_head_dim(head_dim) || block_size != kBlockSize)
     return PKV_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads < 1) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
@@ -208,6 +215,21 @@ int pkv_kv_cache_write(const void *k, const void *v, const int64_t *slot_mapping
   const hipError_t e = pkv::launch_kv_write(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_blocks,
                                             num_kv_heads, head_dim, dtype == PKV_BF16,
                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int pkv_kv_cache_write_fp8(const void *k, const void *v, const int64_t *slot_mapping, void *k_cache,
+                           void *v_cache, int64_t num_tokens, int64_t num_blocks, int num_kv_heads,
+                           int head_dim, int block_size, float k_scale, float v_scale, void *stream) {
+  if (!supported_head_dim(head_dim) || block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f && k_scale < 3.0e38f) || !(v_scale > 0.f && v_scale < 3.0e38f)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads < 1) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+  if (num_tokens * num_kv_heads >= kMaxGrid) return PKV_ERR_SHAPE;
+  const hipError_t e = pkv::launch_kv_write_fp8(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_blocks,
+                                                num_kv_heads, head_dim, k_scale, v_scale,
+                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -265,7 +287,8 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   if (!q_lens && (int64_t)num_seqs * max_q_len != total_q) return PKV_ERR_SHAPE;
   if (q_lens && total_q < num_seqs) return PKV_ERR_SHAPE;
 
-  const bool bf16 = dtype == PKV_BF16;
+  const bool bf16 = dtype != PKV_F32;       // the dtype of q and out
+  const bool f8 = dtype == PKV_BF16_FP8KV;
   const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                             head_dim, dtype, q_lens != nullptr, opts);
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return PKV_ERR_WORKSPACE;
@@ -287,6 +310,8 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.part_lse = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
   a.part_o = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
+  // E4M3 pools: the matrix-core persistent schedule only, and no append in this call
+  if (f8 && (pl.path != PKV_PATH_MFMA || !persist || new_k)) return PKV_ERR_UNSUPPORTED;
   a.item_pre = persist ? reinterpret_cast<int32_t *>(ws + pl.off_item_pre) : nullptr;
   a.spill_base = pl.spill_base;
   a.share_waves = pl.grid / 8 * 4;
@@ -309,6 +334,13 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.num_kv_heads = num_kv_heads;
   a.group = num_heads / num_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.v_scale = 1.f;
+  if (f8) {
+    // the pools' scales factor out of the products: K's into the scores, V's into the epilogue
+    const float ks = opts && opts->k_scale > 0.f ? opts->k_scale : 1.f;
+    a.scale_log2 *= ks;
+    a.v_scale = opts && opts->v_scale > 0.f ? opts->v_scale : 1.f;
+  }
   a.part_size = pl.part_size;
   a.num_parts = pl.num_parts;
   a.row_tiles = pl.row_tiles;
@@ -333,7 +365,7 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
     return PKV_ERR_LAUNCH;
   const hipError_t le =
       pl.path == PKV_PATH_MFMA
-          ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, pl.depth, persist, pl.grid, s)
+          ? pkv::launch_decode_mfma(a, head_dim, pl.rows_per_tile, pl.depth, persist, pl.grid, f8, s)
           : pkv::launch_decode_valu(a, bf16, head_dim, pl.rows_per_tile, s);
   if (le != hipSuccess) return PKV_ERR_LAUNCH;
   if (opts && opts->event_main_end &&

@@ -60,6 +60,10 @@ class Spec:
     # partition size the bench times this workload with (0 = library policy)
     partition_size: int = 0
     seed: int = 0
+    # K/V pools of 8-bit E4M3 codes (q, out and new rows stay bf16) standing for code * scale
+    kv_fp8: bool = False
+    k_scale: float = 1.0 / 32
+    v_scale: float = 1.0 / 32
 
 
 # The five named workloads.  Index i is seeded with 1000 + i.
@@ -73,6 +77,11 @@ NAMED: List[Spec] = [
          seed=1003),
     Spec("long_ctx_splitk_bf16", 256, 64, 8, 128, "bf16", ctx=("lognormal", 4096, 0.8, 64, 32768),
          seed=1004),
+    # the same two batches over E4M3 pools (the FP8 KV cache): half the cache bytes
+    Spec("conc32_fp8kv", 32, 32, 8, 128, "bf16", ctx=("uniform", 256, 2048), write_new_token=True, seed=1001,
+         kv_fp8=True),
+    Spec("long_ctx_fp8kv", 256, 64, 8, 128, "bf16", ctx=("lognormal", 4096, 0.8, 64, 32768), seed=1004,
+         kv_fp8=True),
 ]
 
 
@@ -100,6 +109,10 @@ class Workload:
     v_cache: torch.Tensor             # [num_blocks, KVH, D, B]
     new_k: Optional[torch.Tensor]     # [T_new, KVH, D]
     new_v: Optional[torch.Tensor]
+
+    @property
+    def kv_fp8(self) -> bool:
+        return self.spec.kv_fp8
 
     @property
     def num_seqs(self) -> int:
@@ -207,6 +220,19 @@ def _randn(shape, gen: torch.Generator, device, dtype: str, chunk_elems: int = 1
     return out
 
 
+def _randn_fp8(shape, gen: torch.Generator, device, scale: float, chunk_elems: int = 1 << 27) -> torch.Tensor:
+    """E4M3 codes (uint8) of N(0,1) draws divided by `scale`, by torch's float8_e4m3fn conversion
+    (|x / scale| stays far below 448 at the scales used here)."""
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for start in range(0, n, chunk_elems):
+        m = min(chunk_elems, n - start)
+        x = torch.randn(m, generator=gen, device=device, dtype=torch.float32)
+        flat[start:start + m].copy_((x / scale).to(torch.float8_e4m3fn).view(torch.uint8))
+    return out
+
+
 def build(spec_or_index, device="cpu", poison: bool = False) -> Workload:
     """Draw a workload on `device`.
 
@@ -229,8 +255,12 @@ def build(spec_or_index, device="cpu", poison: bool = False) -> Workload:
     S, H, KVH, D, B = spec.num_seqs, spec.num_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
     total_q = int(qlens.sum())
     q = _randn((total_q, H, D), gen, device, spec.dtype)
-    k_cache = _randn((pool, KVH, B, D), gen, device, spec.dtype)
-    v_cache = _randn((pool, KVH, D, B), gen, device, spec.dtype)
+    if spec.kv_fp8:
+        k_cache = _randn_fp8((pool, KVH, B, D), gen, device, spec.k_scale)
+        v_cache = _randn_fp8((pool, KVH, D, B), gen, device, spec.v_scale)
+    else:
+        k_cache = _randn((pool, KVH, B, D), gen, device, spec.dtype)
+        v_cache = _randn((pool, KVH, D, B), gen, device, spec.dtype)
     slot_mapping = new_k = new_v = None
     if spec.write_new_token:
         pos = ctx.astype(np.int64) - 1
@@ -240,7 +270,7 @@ def build(spec_or_index, device="cpu", poison: bool = False) -> Workload:
         new_v = _randn((S, KVH, D), gen, device, spec.dtype)
 
     if poison:
-        nan = float("nan")
+        nan = 0x7F if spec.kv_fp8 else float("nan")          # E4M3's NaN code
         for s in range(S):
             n = int(ctx[s])
             tail = n % B

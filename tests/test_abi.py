@@ -125,6 +125,23 @@ def test_append_argument_validation(lib):
     assert call(None, None, S=0) == 0                          # empty batch: no-op
 
 
+def test_fp8_pool_limits(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+    full = dict(q="p", kc="p", vc="p", bt="p", cl="p", out="p", dt=2, D=128)
+    valu = _lib.DecodeOptions(0, _lib.PATH_VALU, 0, 0, None, None)
+    assert _decode(lib, **full, opts=ctypes.byref(valu)) == -3           # E4M3 pools: matrix cores only
+    grid = _lib.DecodeOptions(0, 0, 0, _lib.SCHEDULE_GRID, None, None)
+    assert _decode(lib, **full, opts=ctypes.byref(grid)) == -3           # ... on the persistent schedule
+    neg = _lib.DecodeOptions(0, 0, 0, 0, None, None, 0, -1.0, 1.0)
+    assert _decode(lib, **full, opts=ctypes.byref(neg)) == -3            # scales > 0 (or 0 = 1)
+    w = lib.pkv_kv_cache_write_fp8
+    assert w(fake, fake, fake, fake, fake, 4, 8, 2, 64, 16, 0.0, 1.0, None) == -3   # write needs scales > 0
+    assert w(fake, fake, fake, fake, fake, 4, 8, 2, 96, 16, 1.0, 1.0, None) == -3
+    assert w(None, fake, fake, fake, fake, 4, 8, 2, 64, 16, 1.0, 1.0, None) == -1
+    assert w(fake, fake, fake, fake, fake, 0, 8, 2, 64, 16, 1.0, 1.0, None) == 0
+    assert lib.pkv_kv_cache_write(fake, fake, fake, fake, fake, 4, 8, 2, 64, 16, 2, None) == -3  # not via plain write
+
+
 def test_probe_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
     assert lib.pkv_probe_page_stream(None, f, 8, 128, f, f, 4, f, None) == -1
