@@ -56,7 +56,8 @@ typedef enum pkv_status {
   PKV_ERR_NULL = -1,        /* a required pointer is NULL */
   PKV_ERR_SHAPE = -2,       /* sizes are inconsistent (e.g. num_heads % num_kv_heads != 0) */
   PKV_ERR_UNSUPPORTED = -3, /* head_dim, block_size, dtype or partition size outside what is built */
-  PKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than pkv_decode_workspace_bytes() */
+  PKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than pkv_decode_workspace_bytes(); in
+                               pkv_blocks.h: the block pool has too few free blocks */
   PKV_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
 } pkv_status;
 

@@ -52,6 +52,27 @@ EXPORTS = {
     "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
                                         _vp]),
     "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
+    "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, _c_i64, _c_int, _c_int, _c_int, _vp]),
+    # host-side block management (include/pkv_blocks.h); handles are opaque pointers
+    "pkv_block_pool_create": (_vp, [ctypes.c_int32]),
+    "pkv_block_pool_destroy": (None, [_vp]),
+    "pkv_block_pool_free_count": (ctypes.c_int32, [_vp]),
+    "pkv_block_refcount": (ctypes.c_int32, [_vp, ctypes.c_int32]),
+    "pkv_seq_create": (_vp, [_vp]),
+    "pkv_seq_destroy": (None, [_vp]),
+    "pkv_seq_length": (_c_i64, [_vp]),
+    "pkv_seq_num_blocks": (ctypes.c_int32, [_vp]),
+    "pkv_seq_block_table": (ctypes.c_int32, [_vp, _vp, ctypes.c_int32]),
+    "pkv_seq_append": (ctypes.c_int32, [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp]),
+    "pkv_seqs_append": (_c_i64, [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_seq_fork": (_vp, [_vp]),
+    "pkv_seq_adopt_prefix": (ctypes.c_int32, [_vp, _vp, ctypes.c_int32]),
+    "pkv_radix_create": (_vp, [_vp]),
+    "pkv_radix_destroy": (None, [_vp]),
+    "pkv_radix_match": (ctypes.c_int32, [_vp, _vp, _c_i64, _vp, ctypes.c_int32]),
+    "pkv_radix_insert": (ctypes.c_int32, [_vp, _vp, _c_i64, _vp]),
+    "pkv_radix_evict": (ctypes.c_int32, [_vp, ctypes.c_int32]),
+    "pkv_radix_cached_blocks": (ctypes.c_int32, [_vp]),
     "pkv_status_string": (ctypes.c_char_p, [_c_int]),
     "pkv_version": (_c_int, []),
 }

@@ -197,7 +197,7 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_NULL: return "a required pointer is NULL";
     case PKV_ERR_SHAPE: return "inconsistent sizes";
     case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype, path or partition size";
-    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small, or too few free blocks";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
