@@ -50,6 +50,12 @@ def algorithmic_bytes(w) -> int:
     return int(kv + qo + meta)
 
 
+def logical_kv_bytes(w) -> int:
+    """K/V bytes when every sequence reads its own pages (shared pages counted once per reader)."""
+    ekv = 1 if w.kv_fp8 else (4 if w.spec.dtype == "f32" else 2)
+    return int(w.context_lens.astype(np.int64).sum()) * w.spec.num_kv_heads * w.spec.head_dim * 2 * ekv
+
+
 def write_bytes(w) -> int:
     if w.slot_mapping is None:
         return 0
@@ -303,6 +309,10 @@ def main():
     ap.add_argument("--append", default="fused", choices=["fused", "slots"],
                     help="appending workloads: write the new tokens inside the decode call (fused) or "
                          "with pkv_kv_cache_write through slot_mapping first (slots)")
+    ap.add_argument("--prefix-mode", default="auto", choices=["auto", "once", "per-seq", "off"],
+                    help="shared-prefix workloads: pkv_paged_attn_decode_shared_prefix with the library's "
+                         "policy (auto), forced read-once (once) or per-sequence (per-seq); off: plain "
+                         "pkv_paged_attn_decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -393,6 +403,29 @@ def main():
         r = i % R
         dstep(kcs[r], vcs[r], events=events)
 
+    prefix_call = spec.shared_prefix_blocks > 0 and args.prefix_mode != "off"
+    prefix_mode = {"auto": _lib.PREFIX_AUTO, "once": _lib.PREFIX_READ_ONCE,
+                   "per-seq": _lib.PREFIX_PER_SEQUENCE, "off": None}[args.prefix_mode]
+    if prefix_call:
+        # shared-prefix decode: all sequences form one group over their shared prefix blocks
+        if w.slot_mapping is not None:
+            raise SystemExit("shared-prefix workloads append nothing")
+        pre_tokens = spec.shared_prefix_blocks * spec.block_size
+        gs, pl, pb = W.share_prefixes(w, [(0, w.num_seqs, pre_tokens)])
+        meta = w.device_meta(dev)
+        gdev = [torch.from_numpy(a).to(dev) for a in (gs, pl, pb)]
+        pws = _lib.new_workspace(_lib.shared_prefix_workspace_bytes(
+            w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, code, 1, w.num_seqs, pre_tokens,
+            partition_size=P, depth=args.depth, schedule=sched, wgs_per_cu=args.wgs_per_cu), dev)
+
+        def step(i, events=None):
+            r = i % R
+            _lib.paged_attn_decode_shared_prefix(
+                w.q, kcs[r], vcs[r], meta["block_tables"], meta["context_lens"], q_lens, out, lse, H, KVH, D,
+                spec.block_size, w.scale, w.max_context_len, gdev[0], gdev[1], gdev[2], w.num_seqs, pre_tokens,
+                max_q_len=w.max_q_len, partition_size=P, workspace=pws, events=None, depth=args.depth,
+                schedule=sched, wgs_per_cu=args.wgs_per_cu, mode=prefix_mode)
+
     # eager: every step is two C calls from Python; HIP events around the partition kernel
     for i in range(args.warmup):
         step(i)
@@ -408,7 +441,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     eager_ms_step = t_start.elapsed_time(t_end) / args.steps
-    k_ms = float(np.mean([elapsed_ms(b, e) for b, e in ev]))
+    k_ms = None if prefix_call else float(np.mean([elapsed_ms(b, e) for b, e in ev]))
     for b, e in ev:
         hip.hipEventDestroy(b)
         hip.hipEventDestroy(e)
@@ -448,9 +481,14 @@ def main():
     step_bytes = dec_bytes + write_bytes(w)
     tokens = int(w.context_lens.astype(np.int64).sum())
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    if prefix_call:
+        # several kernels share the step (prep, shared-prefix pass, suffix decode and its combine,
+        # merge): the roofline line covers the whole step
+        kernel, k_ms = "shared-prefix step (pkv_paged_attn_decode_shared_prefix, all kernels)", ms_step
     achieved = dec_bytes / (k_ms * 1e-3) / 1e9
     sched_name = ["", "grid", "persistent"][plan["schedule"]]
-    traffic = measured_traffic(spec.name, kernel.split("_")[1], sched_name, P_used, plan["pipeline_depth"])
+    traffic = None if prefix_call else measured_traffic(spec.name, kernel.split("_")[1], sched_name, P_used,
+                                                       plan["pipeline_depth"])
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + attended tokens/s, 1 GPU",
         "value": round(value, 2),
@@ -473,10 +511,13 @@ def main():
             "appends_new_token": w.slot_mapping is not None,
             "append": (append_mode if w.slot_mapping is not None else None),
             "kv_cache": "e4m3" if spec.kv_fp8 else spec.dtype,
+            "shared_prefix_call": prefix_call,
+            "prefix_mode": args.prefix_mode if prefix_call else None,
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
+        "logical_kv_bytes_per_step": logical_kv_bytes(w),
         "step_timing": timing,
         "eager_ms_per_step": round(eager_ms_step, 5),
         "eager_host_us_per_step": round(host_enqueue / args.steps * 1e6, 2),
@@ -494,7 +535,7 @@ def main():
             "algorithmic_bytes_per_launch": dec_bytes,
         },
     }
-    if plan["schedule"] == 2 and not args.no_ceiling:
+    if plan["schedule"] == 2 and not args.no_ceiling and not prefix_call:
         t_probe, pages = pattern_ceiling(w, plan, kcs, vcs)
         ceil = dec_bytes / t_probe / 1e9
         res["roofline"]["pattern_ceiling"] = {

@@ -98,7 +98,15 @@ typedef struct pkv_decode_options {
                                (0 = policy) */
   float k_scale;            /* PKV_BF16_FP8KV: the K pool's scale (0 = 1); ignored otherwise */
   float v_scale;            /* PKV_BF16_FP8KV: the V pool's scale (0 = 1); ignored otherwise */
+  int shared_prefix_mode;   /* pkv_paged_attn_decode_shared_prefix only (pkv_prefix.h): a
+                               pkv_shared_prefix_mode */
 } pkv_decode_options;
+
+typedef enum {
+  PKV_PREFIX_AUTO = 0,          /* read shared prefixes once when the bytes that saves are large */
+  PKV_PREFIX_READ_ONCE = 1,     /* always attend each group's shared prefix once for the group */
+  PKV_PREFIX_PER_SEQUENCE = 2   /* every sequence reads its own pages (pkv_paged_attn_decode) */
+} pkv_shared_prefix_mode;
 
 /*
  * Slot-mapped KV append (lfm25-inference, "Runtime Design": engine-owned KV pages; inferd follow-up

@@ -177,6 +177,69 @@ def lse_combine(outs, lses):
     return out, lse
 
 
+def shared_len(context_len, q_len, group_prefix, block_size=16):
+    """Keys of a group member read through the group's shared blocks: the group's prefix, cut to the
+    whole pages before the member's new tokens (those tokens are its own, never shared)."""
+    return min(int(group_prefix), (int(context_len) - int(q_len)) // block_size * block_size)
+
+
+def shared_prefix_attention(q, k_cache, v_cache, block_tables, context_lens, q_lens, scale, num_kv_heads,
+                            group_starts, prefix_lens, prefix_blocks, block_size=16):
+    """Decode attention computed the read-once way (lfm25-inference, "Runtime Design": prefix reuse
+    through a radix tree, and the log-sum-exp merge of split-K parts): for each group of consecutive
+    sequences, the query rows of all members attend the group's shared blocks in one product (member
+    s sees its first P_s keys there, P_s = shared_len), each sequence attends its keys P_s .. ctx - 1
+    through its own block table, and the two parts merge with lse_combine.  Sequences outside every
+    group have P_s = 0.  Returns (out, lse) like paged_decode_attention, which it equals up to
+    rounding: a softmax over a key set is the merge of softmaxes over any partition of it."""
+    q = np.asarray(q)
+    total_q, H, D = q.shape
+    KVH = int(num_kv_heads)
+    G = H // KVH
+    S = len(context_lens)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(q_lens)])
+    P = np.zeros(S, dtype=np.int64)
+    owner = np.full(S, -1)
+    for g in range(len(prefix_lens)):
+        for s in range(int(group_starts[g]), int(group_starts[g + 1])):
+            owner[s] = g
+            P[s] = shared_len(context_lens[s], q_lens[s], prefix_lens[g], block_size)
+    pre_o = np.zeros((total_q, H, D))
+    pre_l = np.full((total_q, H), -np.inf)
+    # the shared part: one product per (group, kv head) over the stacked rows of its members
+    for g in range(len(prefix_lens)):
+        members = [s for s in range(int(group_starts[g]), int(group_starts[g + 1])) if P[s] > 0]
+        if not members:
+            continue
+        pg = int(prefix_lens[g])
+        for kv in range(KVH):
+            K, V = gather_kv(k_cache, v_cache, prefix_blocks[g], pg, kv, block_size)
+            rows, last, where = [], [], []
+            for s in members:
+                for i in range(int(q_lens[s])):
+                    for h in range(kv * G, (kv + 1) * G):
+                        rows.append(widen(q[starts[s] + i, h]))
+                        last.append(P[s] - 1)
+                        where.append((starts[s] + i, h))
+            o, l = attend(np.stack(rows), K, V, scale, np.asarray(last))
+            for r, (row, h) in enumerate(where):
+                pre_o[row, h], pre_l[row, h] = o[r], l[r]
+    # each sequence's own keys
+    suf_o = np.zeros((total_q, H, D))
+    suf_l = np.full((total_q, H), -np.inf)
+    for s in range(S):
+        n, qs, base, ps = int(context_lens[s]), int(q_lens[s]), int(starts[s]), int(P[s])
+        last = n - qs + np.arange(qs) - ps
+        for kv in range(KVH):
+            K, V = gather_kv(k_cache, v_cache, block_tables[s], n, kv, block_size)
+            rows = widen(q[base:base + qs, kv * G:(kv + 1) * G, :]).reshape(qs * G, D)
+            o, l = attend(rows, K[ps:], V[ps:], scale, np.repeat(last, G))
+            suf_o[base:base + qs, kv * G:(kv + 1) * G] = o.reshape(qs, G, D)
+            suf_l[base:base + qs, kv * G:(kv + 1) * G] = l.reshape(qs, G)
+    return lse_combine([pre_o, suf_o], [pre_l, suf_l])
+
+
 def kv_cache_write(k_cache, v_cache, k, v, slot_mapping, block_size=16):
     """Slot-mapped append: new row t goes to physical slot slot_mapping[t] = block * B + offset, i.e.
     k_cache[block, :, offset, :] = k[t] and v_cache[block, :, :, offset] = v[t]; a negative slot

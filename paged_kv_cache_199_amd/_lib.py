@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libpkv.so")
 PKV_F32, PKV_BF16, PKV_BF16_FP8KV = 0, 1, 2
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_GRID, SCHEDULE_PERSISTENT = 0, 1, 2
+PREFIX_AUTO, PREFIX_READ_ONCE, PREFIX_PER_SEQUENCE = 0, 1, 2
 BLOCK_SIZE = 16
 
 _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
@@ -26,7 +27,8 @@ _c_int, _c_i64, _c_sz, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 class DecodeOptions(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("path", _c_int), ("pipeline_depth", _c_int),
                 ("schedule", _c_int), ("event_main_begin", _vp), ("event_main_end", _vp),
-                ("workgroups_per_cu", _c_int), ("k_scale", _c_f), ("v_scale", _c_f)]
+                ("workgroups_per_cu", _c_int), ("k_scale", _c_f), ("v_scale", _c_f),
+                ("shared_prefix_mode", _c_int)]
 
 
 class DecodePlanInfo(ctypes.Structure):
@@ -52,6 +54,12 @@ EXPORTS = {
     "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
                                         _vp]),
     "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
+    "pkv_decode_shared_prefix_workspace_bytes": (_c_sz, [_c_int] * 11 + [ctypes.POINTER(DecodeOptions)]),
+    "pkv_paged_attn_decode_shared_prefix": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                                     _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
+                                                     _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                                     ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, _c_i64, _c_int, _c_int, _c_int, _vp]),
     # host-side block management (include/pkv_blocks.h); handles are opaque pointers
     "pkv_block_pool_create": (_vp, [ctypes.c_int32]),
@@ -278,6 +286,67 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                                           float(scale), code, ctypes.byref(o), _ptr(workspace), ws_bytes,
                                           _stream(stream))
     _check(rc, "pkv_paged_attn_decode_append")
+
+
+def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                                    num_heads, num_kv_heads, head_dim, block_size, scale, max_context_len,
+                                    group_starts, prefix_lens, prefix_blocks, max_group_size, max_prefix_len,
+                                    max_q_len: int = 1, partition_size: int = 0, workspace=None, events=None,
+                                    stream=None, depth: int = 0, schedule: int = 0, wgs_per_cu: int = 0,
+                                    k_scale: float = 0.0, v_scale: float = 0.0, mode: int = PREFIX_AUTO) -> None:
+    """Decode attention reading each group's shared prefix once (include/pkv_prefix.h).
+
+    group_starts int32 [G+1], prefix_lens int32 [G] and prefix_blocks int32 [G, max_prefix_len / 16]
+    on the GPU describe the groups; max_group_size / max_prefix_len are host-known bounds.  Other
+    arguments as paged_attn_decode (bf16 q/out over bf16 or E4M3 pools)."""
+    lib = load()
+    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
+    total_q = q.shape[0]
+    S = context_lens.numel()
+    NB = k_cache.shape[0]
+    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
+    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    code = _decode_code(q, k_cache, v_cache, out)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
+          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
+    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
+    if q_lens is not None:
+        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
+              "lse: fp32 [total_q, H]")
+    G = 0 if group_starts is None else group_starts.numel() - 1
+    if G > 0:
+        for t in (group_starts, prefix_lens, prefix_blocks):
+            _need(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda, "group arrays: int32, contiguous, GPU")
+        _need(prefix_lens.numel() == G and tuple(prefix_blocks.shape) == (G, max_prefix_len // block_size),
+              "prefix_lens [G], prefix_blocks [G, max_prefix_len / 16]")
+    o = _opts(partition_size, PATH_AUTO, events, depth, schedule, wgs_per_cu, k_scale, v_scale)
+    o.shared_prefix_mode = mode
+    need = int(lib.pkv_decode_shared_prefix_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
+                                                             num_kv_heads, head_dim, code, max(G, 0),
+                                                             max_group_size, max_prefix_len, ctypes.byref(o)))
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.pkv_paged_attn_decode_shared_prefix(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(q_lens), _ptr(out),
+        _ptr(lse), S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB, num_heads, num_kv_heads,
+        head_dim, block_size, float(scale), code, _ptr(group_starts if G > 0 else None),
+        _ptr(prefix_lens if G > 0 else None), _ptr(prefix_blocks if G > 0 else None), max(G, 0), max_group_size,
+        max_prefix_len, ctypes.byref(o), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "pkv_paged_attn_decode_shared_prefix")
+
+
+def shared_prefix_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                                  head_dim, dtype_code, num_groups, max_group_size, max_prefix_len,
+                                  partition_size=0, depth=0, schedule=0, wgs_per_cu=0) -> int:
+    o = DecodeOptions(partition_size, PATH_AUTO, depth, schedule, None, None, wgs_per_cu)
+    return int(load().pkv_decode_shared_prefix_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len,
+                                                               num_heads, num_kv_heads, head_dim, dtype_code,
+                                                               num_groups, max_group_size, max_prefix_len,
+                                                               ctypes.byref(o)))
 
 
 class DecodeStep:

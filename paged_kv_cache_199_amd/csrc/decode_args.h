@@ -46,6 +46,30 @@ struct DecodeArgs {
   const void *new_v;
 };
 
+// Read-once decode over shared prefixes: groups of consecutive sequences whose first tokens sit in
+// the group's shared physical blocks.
+constexpr int kPrefixRows = 32;   // rows per prefix wave: two 16-row matrix-core tiles
+struct PrefixArgs {
+  const int32_t *group_starts;   // [num_groups + 1]
+  const int32_t *prefix_lens;    // [num_groups]
+  const int32_t *prefix_blocks;  // [num_groups, max_prefix_len / 16]
+  int num_groups;
+  int max_group_size;
+  int max_prefix_len;            // a multiple of 16
+  int rows_max;                  // max_group_size * max_q_len * G
+  int row_tiles;                 // ceil(rows_max / 32)
+  int chunk_pages;
+  int chunks;                    // ceil(max_prefix_len / 16 / chunk_pages)
+  int32_t *skip;                 // [num_seqs]: P_s
+  int32_t *sfx_ctx;              // [num_seqs]: context_lens - P_s
+  int32_t *sfx_table;            // [num_seqs, sfx_stride]
+  int sfx_stride;                // ceil(max_context_len / 16)
+  const int32_t *q_start;        // NULL: s * max_q_len
+  float *sfx_lse;                // [total_q, H], natural log, written by the suffix pass
+  float *pre_o;                  // [items * 32, D]
+  float *pre_lse;                // [items * 32], log2
+};
+
 // Per-unit sequence facts with the clamps that keep bad metadata memory-safe.
 struct SeqInfo {
   int ctx;      // context length, clamped to the table width and max_context_len

@@ -77,6 +77,10 @@ NAMED: List[Spec] = [
          seed=1003),
     Spec("long_ctx_splitk_bf16", 256, 64, 8, 128, "bf16", ctx=("lognormal", 4096, 0.8, 64, 32768),
          seed=1004),
+    # a system-prompt-heavy batch: 64 requests behind one 4096-token shared prefix, private tails of
+    # 128..1024 tokens (the read-once decode's case; a stand-in sized for this chip)
+    Spec("shared_prefix_64x4k_bf16", 64, 32, 8, 128, "bf16", ctx=("uniform", 4096 + 128, 4096 + 1024),
+         shared_prefix_blocks=256, seed=1005),
     # the same two batches over E4M3 pools (the FP8 KV cache): half the cache bytes
     Spec("conc32_fp8kv", 32, 32, 8, 128, "bf16", ctx=("uniform", 256, 2048), write_new_token=True, seed=1001,
          kv_fp8=True),
@@ -295,3 +299,35 @@ def custom(name: str, ctx: Sequence[int], q_len=1, num_heads=8, num_kv_heads=2, 
     """Spec for an explicit list of context lengths (edge-case parity runs)."""
     return Spec(name, len(ctx), num_heads, num_kv_heads, head_dim, dtype, ctx=list(ctx),
                 q_len=q_len, seed=seed, **kw)
+
+
+def share_prefixes(w: Workload, groups):
+    """Make consecutive sequences share prefix blocks: groups = [(first, end, prefix_tokens)], prefix
+    a multiple of 16.  Each group takes its prefix ids from its longest member (cut to that member's
+    blocks) and every member's table points its leading blocks (as many as it has, up to the prefix)
+    at them.  Rewrites w.block_tables in place; returns (group_starts [n+1], prefix_lens [n],
+    prefix_blocks [n, max prefix blocks]) int32 arrays describing the groups."""
+    B = w.spec.block_size
+    nblk = (w.context_lens.astype(np.int64) + B - 1) // B
+    starts, lens, rows = [], [], []
+    for first, end, prefix in groups:
+        assert prefix % B == 0 and 0 <= first <= end <= w.num_seqs
+        members = list(range(first, end))
+        donor = max(members, key=lambda s: int(nblk[s])) if members else first
+        pb = min(prefix // B, int(nblk[donor])) if members else 0
+        ids = w.block_tables[donor, :pb].copy()
+        for s in members:
+            k = min(int(nblk[s]), pb)
+            w.block_tables[s, :k] = ids[:k]
+        if starts and starts[-1] != first:
+            raise ValueError("groups must be consecutive")
+        if not starts:
+            starts.append(first)
+        starts.append(end)
+        lens.append(pb * B)
+        rows.append(ids)
+    width = max([len(r) for r in rows] + [1])
+    blocks = np.zeros((len(rows), width), dtype=np.int32)
+    for g, r in enumerate(rows):
+        blocks[g, :len(r)] = r
+    return np.asarray(starts, dtype=np.int32), np.asarray(lens, dtype=np.int32), blocks

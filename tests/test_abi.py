@@ -142,6 +142,30 @@ def test_fp8_pool_limits(lib):
     assert lib.pkv_kv_cache_write(fake, fake, fake, fake, fake, 4, 8, 2, 64, 16, 2, None) == -3  # not via plain write
 
 
+def test_shared_prefix_argument_validation(lib):
+    f = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+
+    def call(dt=1, ng=1, mgs=4, mpl=512, gs=f, pl=f, pb=f, S=4, D=64, ws=None, wsb=0, q=f):
+        return lib.pkv_paged_attn_decode_shared_prefix(q, f, f, f, f, None, f, None, S, 64, S, 1, 1024, 64, 8, 2, D,
+                                                       16, 0.125, dt, gs, pl, pb, ng, mgs, mpl, None, ws, wsb, None)
+    assert call(dt=0) == -3                          # fp32: the matrix-core kernels only
+    assert call(mpl=500) == -3                       # prefix bound in whole pages
+    assert call(ng=-1) == -2 and call(mgs=0) == -2
+    assert call(q=None) == -1 and call(gs=None) == -1 and call(pb=None) == -1
+    assert call(D=96) == -3
+    assert call() == -4                              # the workspace is required
+    assert call(S=0, q=None) == 0                    # empty batch: no-op
+    assert call(ng=0, gs=None, pl=None, pb=None) == -4   # no groups: still needs the suffix pass workspace
+    bad = _lib.DecodeOptions(0, 0, 0, 0, None, None, 0, 0.0, 0.0, 3)
+    assert lib.pkv_paged_attn_decode_shared_prefix(f, f, f, f, f, None, f, None, 4, 64, 4, 1, 1024, 64, 8, 2, 64, 16,
+                                                   0.125, 1, f, f, f, 1, 4, 512, ctypes.byref(bad), None, 0,
+                                                   None) == -3                  # unknown shared_prefix_mode
+    need = lib.pkv_decode_shared_prefix_workspace_bytes(4, 4, 1, 1024, 8, 2, 64, 1, 1, 4, 512, None)
+    plain = lib.pkv_decode_workspace_bytes(4, 4, 1, 1024, 8, 2, 64, 1, None)
+    assert need > plain > 0
+    assert lib.pkv_decode_shared_prefix_workspace_bytes(4, 4, 1, 1024, 8, 2, 64, 0, 1, 4, 512, None) == 0
+
+
 def test_probe_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
     assert lib.pkv_probe_page_stream(None, f, 8, 128, f, f, 4, f, None) == -1
