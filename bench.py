@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -291,6 +292,112 @@ def bench_blocks(args, dev):
     print(json.dumps(res), flush=True)
 
 
+def prefill_flops(w) -> int:
+    """Matrix products of the attention: 2 D flops for q.k and 2 D for p.v per (query row, head,
+    visible key); row i of a q-token chunk sees ctx - q + i + 1 keys."""
+    ctx = w.context_lens.astype(np.int64)
+    q = w.q_lens.astype(np.int64)
+    pairs = int((q * (ctx - q) + q * (q + 1) // 2).sum())
+    return pairs * w.spec.num_heads * 4 * w.spec.head_dim
+
+
+def bench_prefill(args, dev, spec):
+    """Chunked prefill: pkv_paged_attn_prefill over the workload's chunks, timed as a HIP graph of K
+    steps; the roofline is the matrix cores' dense bf16 peak."""
+    import torch
+
+    from paged_kv_cache_199_amd import _lib
+    from paged_kv_cache_199_amd import workloads as W
+
+    w = W.build(spec, dev)
+    meta = w.device_meta(dev)
+    H, KVH, D = spec.num_heads, spec.num_kv_heads, spec.head_dim
+    out = torch.empty_like(w.q)
+    lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
+    q_lens = None if w.uniform_q else meta["q_lens"]
+
+    def step():
+        _lib.paged_attn_prefill(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"], q_lens, out,
+                                lse, H, KVH, D, spec.block_size, w.scale, w.max_context_len, w.max_q_len)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(args.steps):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    kv = algorithmic_bytes(w)
+    res = {
+        "metric": "paged prefill attention TFLOP/s (% of bf16 MFMA peak) + new tokens/s, 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V, shuffled 16-token pages)",
+        "config": {"workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
+                   "head_dim": D, "block_size": spec.block_size, "new_tokens": int(w.q_lens.sum()),
+                   "context_tokens": int(w.context_lens.astype(np.int64).sum()),
+                   "max_context_len": w.max_context_len},
+        "new_tokens_per_s": round(int(w.q_lens.sum()) / (ms * 1e-3), 1),
+        "kv_bytes_per_step": kv,
+        "eager_ms_per_step": round(eager_ms, 5),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_mfma_kernel", "kernel_ms": round(ms, 5), "flops_per_launch": flops},
+    }
+    if args.cpu_budget > 0:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import paged_attention as O
+
+        def bits(t):
+            t = t.detach().cpu().contiguous()
+            return t.view(torch.int16).numpy().view(np.uint16)
+
+        qh, kc, vc = bits(w.q), bits(w.k_cache), bits(w.v_cache)
+        done, t_used, n = 0, 0.0, 0
+        with threadpool_limits(limits=1):
+            while t_used < min(args.cpu_budget, 20.0):
+                s_ = n % w.num_seqs
+                t0 = time.perf_counter()
+                O.paged_decode_attention(qh, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale, KVH,
+                                         spec.block_size, seqs=[s_])
+                t_used += time.perf_counter() - t0
+                c, qq = int(w.context_lens[s_]), int(w.q_lens[s_])
+                done += (qq * (c - qq) + qq * (qq + 1) // 2) * H * 4 * D
+                n += 1
+        res["cpu_baseline"] = {"value": round(done / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} whole sequences of the workload (all heads), numpy float64, "
+                                         f"1 BLAS thread, {t_used:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +453,9 @@ def main():
         return
 
     spec = W.named(args.workload)
+    if spec.prefill:
+        bench_prefill(args, dev, spec)
+        return
     P = spec.partition_size if args.partition_size < 0 else args.partition_size
     path = {"auto": _lib.PATH_AUTO, "valu": _lib.PATH_VALU, "mfma": _lib.PATH_MFMA}[args.path]
     w = W.build(spec, dev)

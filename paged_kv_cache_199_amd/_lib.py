@@ -60,6 +60,8 @@ EXPORTS = {
                                                      _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                                      _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                                      ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
+    "pkv_paged_attn_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, _c_i64, _c_int, _c_int, _c_int, _vp]),
     # host-side block management (include/pkv_blocks.h); handles are opaque pointers
     "pkv_block_pool_create": (_vp, [ctypes.c_int32]),
@@ -337,6 +339,34 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_l
         _ptr(prefix_lens if G > 0 else None), _ptr(prefix_blocks if G > 0 else None), max(G, 0), max_group_size,
         max_prefix_len, ctypes.byref(o), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_paged_attn_decode_shared_prefix")
+
+
+def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
+                       num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len, stream=None) -> None:
+    """Prefill / chunked-prefill attention through the C ABI (include/pkv_prefill.h): bf16 q/out
+    [total_q, H, D] over bf16 pools; the new tokens' K/V already written to the cache."""
+    lib = load()
+    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
+    total_q = q.shape[0]
+    S = context_lens.numel()
+    NB = k_cache.shape[0]
+    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
+    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    code = _decode_code(q, k_cache, v_cache, out)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
+          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
+    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
+    if q_lens is not None:
+        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
+              "lse: fp32 [total_q, H]")
+    rc = lib.pkv_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                    _ptr(q_lens), _ptr(out), _ptr(lse), S, block_tables.shape[1], total_q, max_q_len,
+                                    max_context_len, NB, num_heads, num_kv_heads, head_dim, block_size,
+                                    float(scale), code, _stream(stream))
+    _check(rc, "pkv_paged_attn_prefill")
 
 
 def shared_prefix_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,

@@ -17,7 +17,7 @@ ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
            "decode_combine.hip", "stream_probe.hip", "block_manager.hip",
-           "decode_prefix.hip"]
+           "decode_prefix.hip", "prefill_mfma.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/pkv.h: argument validation, the split-K / kernel policy,
 // workspace carving and kernel launches.  Nothing here allocates, synchronizes or reads device memory.
 #include "../../include/pkv.h"
+#include "../../include/pkv_prefill.h"
 #include "../../include/pkv_prefix.h"
 
 #include <hip/hip_runtime.h>
@@ -29,6 +30,7 @@ hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStr
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st);
 hipError_t launch_prefix_merge(const DecodeArgs &a, const PrefixArgs &p, int head_dim, hipStream_t st);
+hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, hipStream_t st);
 }  // namespace pkv
 
 namespace {
@@ -606,6 +608,58 @@ int pkv_paged_attn_decode_shared_prefix(const void *q, const void *k_cache, cons
   if (rc != PKV_OK) return rc;
   if (pkv::launch_prefix_merge(a, p, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
   return PKV_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int pkv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, const int32_t *q_lens, void *out, float *lse, int num_seqs,
+                           int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
+                           int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           float scale, int dtype, void *stream) {
+  if (block_size != kBlockSize || dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                              dtype, nullptr);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_ERR_NULL;
+  if (max_blocks_per_seq < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
+  if (!q_lens && (int64_t)num_seqs * max_q_len != total_q) return PKV_ERR_SHAPE;
+  if (q_lens && total_q < num_seqs) return PKV_ERR_SHAPE;
+  const int G = num_heads / num_kv_heads;
+  const int64_t row_blocks = ceil_div((int64_t)max_q_len * G, 128);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * row_blocks;
+  if (units + 8 >= kMaxGrid) return PKV_ERR_SHAPE;
+
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.q_lens = q_lens;
+  a.out = out;
+  a.lse = lse;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.max_context_len = max_context_len;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = G;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.v_scale = 1.f;
+  a.part_size = max_context_len;
+  a.num_parts = 1;
+  a.row_tiles = (int)row_blocks;
+  a.units = (int)units;
+  a.per_xcd = ceil_div(units, 8);
+  return pkv::launch_prefill_mfma(a, head_dim, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                                : PKV_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -1,0 +1,152 @@
+// Paged prefill / chunked prefill attention on the matrix cores (bf16).
+//
+// The same operation as decode (every new token of a sequence attends the cached tokens and the new
+// tokens up to itself, through the block table), with many new tokens per sequence: a prompt, or a
+// chunk of one appended to an existing context.  The lfm25-inference page pairs paged decode with
+// ragged prefill over the same cache ("Runtime Design"); the inferd page lists the persistent
+// paged cache and a real paged-attention kernel among its follow-up plans.
+//
+// With hundreds of query rows per (sequence, kv head) the products are dense enough for the matrix
+// cores to be the bound, and the K/V pages are reused by every row tile.  So:
+//  * one workgroup per (sequence, kv head, block of 128 rows); rows = new tokens x the G query heads
+//    of the kv head, in token order; each of its 4 waves owns 32 rows (two 16-row MFMA tiles);
+//  * every K/V page is fetched once per workgroup, staged in LDS four pages at a time (double-
+//    buffered: the next four pages' loads fly while these are computed) and read by all four waves;
+//  * a workgroup stops at the page holding its last row's last visible key (causal), and a wave
+//    skips the pages past its own rows' limit;
+//  * per page, each wave runs the decode's matrix-core step (scores, mask, online softmax, P.V);
+//    rows end with their final output and natural-log LSE (no split: there are enough workgroups).
+// Work units are laid out row block fastest and spread over the XCDs in contiguous ranges, so the
+// workgroups that read one (sequence, kv head)'s pages share an L2.
+#include "mfma_wave.h"
+
+namespace pkv {
+
+constexpr int kPrefillRows = 128;   // rows per workgroup
+
+template <int D, int SP>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
+  constexpr int NT = 2;
+  constexpr int ROWB = D * 2;
+  constexpr int KPAD = ROWB + 16;            // LDS row stride of a K page (breaks bank aliasing)
+  constexpr int KBYTES = kBlock * KPAD;
+  constexpr int VBYTES = kBlock * ROWB;      // V page [D][16] as in HBM
+  constexpr int PBYTES = KBYTES + VBYTES;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int CH = ROWB / 16;              // 16-byte chunks per K row
+  // two stages of SP pages: the next stage's loads fly while this stage is computed
+  __shared__ __attribute__((aligned(16))) char lds[2][SP][PBYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  int u = xcd_unit(blockIdx.x, a.per_xcd);
+  if (u >= a.units) return;
+  const int rb = u % a.row_tiles;
+  u /= a.row_tiles;
+  const int kvh = u % a.num_kv_heads;
+  const int s = u / a.num_kv_heads;
+
+  // q rows before sequence s (the workgroup sums q_lens itself: no workspace)
+  SeqInfo si = load_seq(a, s);
+  if (a.q_lens) {
+    __shared__ int part[4];
+    int acc = 0;
+    for (int t = tid; t < s; t += 256) acc += max(a.q_lens[t], 0);
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    si.qbase = part[0] + part[1] + part[2] + part[3];
+  }
+  const int G = a.group;
+  const int rows = si.qs * G;
+  const int wg_row0 = rb * kPrefillRows;
+  if (wg_row0 >= rows || si.ctx <= 0) return;
+  const int row0 = wg_row0 + wave * 32;
+  // the pages this workgroup reads: up to its last row's last visible key
+  const int wg_last_tok = (min(rows, wg_row0 + kPrefillRows) - 1) / G;
+  const int npages = (si.ctx - si.qs + wg_last_tok) / kBlock + 1;
+  const int my_pages = row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + 32) - 1) / G) / kBlock + 1 : 0;
+  const int nstages = (npages + SP - 1) / SP;
+
+  WaveRows<D, NT> w;
+  load_rows<D, NT>(a, si, kvh, row0, rows, col, grp, w);
+  WaveAcc<D, NT> st;
+  init_acc<D, NT>(st);
+
+  const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  const int64_t page_bytes = (int64_t)kBlock * ROWB;
+  // each thread moves one 16-byte chunk of every K page and one of every V page (D = 64: threads < 128)
+  const bool mover = tid < kBlock * CH;
+  uint4 kn[SP], vn[SP];
+  int okn = 0;                               // bit p: page p of the stage has a valid id
+  auto fetch = [&](int stage) {
+    okn = 0;
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = min(stage * SP + p, npages - 1);   // past the end: re-read the last page
+      const int bid = bt[j];
+      const bool ok = bid >= 0 && bid < a.num_blocks;
+      okn |= ok ? 1 << p : 0;
+      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * 16;
+      if (mover) {
+        kn[p] = ld16(kbase + off);
+        vn[p] = ld16(vbase + off);
+      }
+    }
+  };
+  auto stage_to = [&](int b) {
+    if (mover) {
+      #pragma unroll
+      for (int p = 0; p < SP; ++p) {
+        *reinterpret_cast<uint4 *>(&lds[b][p][(tid / CH) * KPAD + (tid % CH) * 16]) = kn[p];
+        *reinterpret_cast<uint4 *>(&lds[b][p][KBYTES + tid * 16]) = vn[p];
+      }
+    }
+  };
+
+  fetch(0);
+  stage_to(0);
+  int ok_cur = __builtin_amdgcn_readfirstlane(okn);
+  __syncthreads();
+  for (int g = 0; g < nstages; ++g) {
+    const int b = g & 1;
+    if (g + 1 < nstages) fetch(g + 1);
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = g * SP + p;
+      if (j < my_pages) {
+        uint4 kr[NK];
+        uint2 vr[ND];
+        const char *kl = &lds[b][p][col * KPAD + grp * 16];
+        #pragma unroll
+        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
+        const char *vl = &lds[b][p][KBYTES + (col * kBlock + 4 * grp) * 2];
+        #pragma unroll
+        for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * kBlock * 2);
+        mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
+      }
+    }
+    if (g + 1 < nstages) {
+      stage_to(b ^ 1);
+      ok_cur = __builtin_amdgcn_readfirstlane(okn);
+    }
+    __syncthreads();
+  }
+  if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
+}
+
+hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, hipStream_t st) {
+  const dim3 grid((unsigned)(a.per_xcd * 8));
+  if (head_dim == 64) prefill_mfma_kernel<64, 4><<<grid, 256, 0, st>>>(a);
+  else prefill_mfma_kernel<128, 4><<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -64,6 +64,8 @@ class Spec:
     kv_fp8: bool = False
     k_scale: float = 1.0 / 32
     v_scale: float = 1.0 / 32
+    # many new tokens per sequence: timed through the prefill entry point
+    prefill: bool = False
 
 
 # The five named workloads.  Index i is seeded with 1000 + i.
@@ -81,6 +83,9 @@ NAMED: List[Spec] = [
     # 128..1024 tokens (the read-once decode's case; a stand-in sized for this chip)
     Spec("shared_prefix_64x4k_bf16", 64, 32, 8, 128, "bf16", ctx=("uniform", 4096 + 128, 4096 + 1024),
          shared_prefix_blocks=256, seed=1005),
+    # chunked prefill: 16 sequences each appending a 512-token chunk to 0..3584 cached tokens
+    Spec("prefill_chunk_bf16", 16, 32, 8, 128, "bf16", ctx=("uniform", 512, 4096), q_len=512, seed=1006,
+         prefill=True),
     # the same two batches over E4M3 pools (the FP8 KV cache): half the cache bytes
     Spec("conc32_fp8kv", 32, 32, 8, 128, "bf16", ctx=("uniform", 256, 2048), write_new_token=True, seed=1001,
          kv_fp8=True),

@@ -166,6 +166,20 @@ def test_shared_prefix_argument_validation(lib):
     assert lib.pkv_decode_shared_prefix_workspace_bytes(4, 4, 1, 1024, 8, 2, 64, 0, 1, 4, 512, None) == 0
 
 
+def test_prefill_argument_validation(lib):
+    f = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+
+    def call(dt=1, D=128, B=16, S=4, q=f, mq=256, tq=1024):
+        return lib.pkv_paged_attn_prefill(q, f, f, f, f, None, f, None, S, 64, tq, mq, 1024, 64, 32, 8, D, B, 0.1, dt,
+                                          None)
+    assert call(dt=0) == -3 and call(dt=2) == -3      # bf16 pools only
+    assert call(D=96) == -3 and call(B=8) == -3
+    assert call(q=None) == -1
+    assert call(tq=1000) == -2                        # q_lens NULL: total_q = num_seqs * max_q_len
+    assert call(mq=2048) == -2                        # max_q_len <= max_context_len
+    assert call(S=0, q=None) == 0
+
+
 def test_probe_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
     assert lib.pkv_probe_page_stream(None, f, 8, 128, f, f, 4, f, None) == -1
