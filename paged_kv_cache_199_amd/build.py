@@ -20,14 +20,16 @@ SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_mfma.
            "decode_prefix.hip", "prefill_mfma.hip"]
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core accumulators in ordinary VGPRs: the softmax rescale then needs no AGPR copies
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# matrix-core accumulators in ordinary VGPRs (the softmax rescale then needs no AGPR copies), except
+# where a wave's accumulators outgrow the VGPRs
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC: set = set()
 
 
 def hipcc() -> str:
@@ -37,19 +39,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_library(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(p, verbose):
+    _, stderr = p.communicate()
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    err = "\n".join(l for l in (stderr or "").splitlines() if noise not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({p.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Every source to an object (in parallel), then one shared library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    objs, pending = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        extra = [] if src in AGPR_ACC else VGPR_FORM
+        pending.append([hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+    running = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            running.append(_run(pending.pop(0), verbose))
+        _finish(running.pop(0), verbose)
+    tmp = LIB + ".tmp"
+    p = _run([hipcc(), "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    _finish(p, verbose)
     os.replace(tmp, LIB)
     return LIB
 

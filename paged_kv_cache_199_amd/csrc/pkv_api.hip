@@ -629,7 +629,7 @@ int pkv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cac
   if (!q_lens && (int64_t)num_seqs * max_q_len != total_q) return PKV_ERR_SHAPE;
   if (q_lens && total_q < num_seqs) return PKV_ERR_SHAPE;
   const int G = num_heads / num_kv_heads;
-  const int64_t row_blocks = ceil_div((int64_t)max_q_len * G, 128);
+  const int64_t row_blocks = ceil_div((int64_t)max_q_len * G, 128);   // rows per prefill workgroup
   const int64_t units = (int64_t)num_seqs * num_kv_heads * row_blocks;
   if (units + 8 >= kMaxGrid) return PKV_ERR_SHAPE;
 

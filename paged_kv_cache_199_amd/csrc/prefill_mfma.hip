@@ -9,7 +9,8 @@
 // With hundreds of query rows per (sequence, kv head) the products are dense enough for the matrix
 // cores to be the bound, and the K/V pages are reused by every row tile.  So:
 //  * one workgroup per (sequence, kv head, block of 128 rows); rows = new tokens x the G query heads
-//    of the kv head, in token order; each of its 4 waves owns 32 rows (two 16-row MFMA tiles);
+//    of the kv head, in token order; each of its 4 waves owns 32 rows (two 16-row MFMA tiles), so
+//    two workgroups fit a CU (64 rows per wave, one workgroup per CU, measured slower);
 //  * every K/V page is fetched once per workgroup, staged in LDS four pages at a time (double-
 //    buffered: the next four pages' loads fly while these are computed) and read by all four waves;
 //  * a workgroup stops at the page holding its last row's last visible key (causal), and a wave
@@ -22,15 +23,26 @@
 
 namespace pkv {
 
-constexpr int kPrefillRows = 128;   // rows per workgroup
+#ifndef PKV_PREFILL_KPAD
+#define PKV_PREFILL_KPAD 16   // bytes after each token row of a K page in LDS (a multiple of 16)
+#endif
+#ifndef PKV_PREFILL_VPAD
+#define PKV_PREFILL_VPAD 0    // bytes after each dim row (16 tokens) of a V page in LDS (a multiple of 16)
+#endif
+constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
+
+__device__ __forceinline__ int vswz(int d) { return (d >> 3) & 3; }
+constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
 template <int D, int SP>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
-  constexpr int NT = 2;
+  constexpr int NT = kPrefillNT;
+  constexpr int WROWS = 16 * NT;             // rows per wave
   constexpr int ROWB = D * 2;
-  constexpr int KPAD = ROWB + 16;            // LDS row stride of a K page (breaks bank aliasing)
+  constexpr int KPAD = ROWB + PKV_PREFILL_KPAD;          // LDS row stride of a K page
   constexpr int KBYTES = kBlock * KPAD;
-  constexpr int VBYTES = kBlock * ROWB;      // V page [D][16] as in HBM
+  constexpr int VROW = kBlock * 2 + PKV_PREFILL_VPAD;    // LDS stride of a V dim row (16 tokens)
+  constexpr int VBYTES = D * VROW;                       // V page [D][16]
   constexpr int PBYTES = KBYTES + VBYTES;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
@@ -66,11 +78,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const int rows = si.qs * G;
   const int wg_row0 = rb * kPrefillRows;
   if (wg_row0 >= rows || si.ctx <= 0) return;
-  const int row0 = wg_row0 + wave * 32;
+  const int row0 = wg_row0 + wave * WROWS;
   // the pages this workgroup reads: up to its last row's last visible key
   const int wg_last_tok = (min(rows, wg_row0 + kPrefillRows) - 1) / G;
   const int npages = (si.ctx - si.qs + wg_last_tok) / kBlock + 1;
-  const int my_pages = row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + 32) - 1) / G) / kBlock + 1 : 0;
+  const int my_pages = row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + WROWS) - 1) / G) / kBlock + 1 : 0;
   const int nstages = (npages + SP - 1) / SP;
 
   WaveRows<D, NT> w;
@@ -106,7 +118,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
       #pragma unroll
       for (int p = 0; p < SP; ++p) {
         *reinterpret_cast<uint4 *>(&lds[b][p][(tid / CH) * KPAD + (tid % CH) * 16]) = kn[p];
-        *reinterpret_cast<uint4 *>(&lds[b][p][KBYTES + tid * 16]) = vn[p];
+        // V dim row d keeps its four 4-token groups in slots g ^ vswz(d): the dims a read instruction
+        // pairs up (d and d + 8) then sit in different banks
+        const int d = tid >> 1;
+        const int g0 = ((tid & 1) * 2) ^ vswz(d);
+        char *vrow = &lds[b][p][KBYTES + d * VROW];
+        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(vn[p].x, vn[p].y);
+        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(vn[p].z, vn[p].w);
       }
     }
   };
@@ -127,9 +145,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
         const char *kl = &lds[b][p][col * KPAD + grp * 16];
         #pragma unroll
         for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
-        const char *vl = &lds[b][p][KBYTES + (col * kBlock + 4 * grp) * 2];
+        const char *vl = &lds[b][p][KBYTES + col * VROW];
         #pragma unroll
-        for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * kBlock * 2);
+        for (int t = 0; t < ND; ++t)
+          vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * VROW + (grp ^ vswz(col + 16 * t)) * 8);
         mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
       }
     }
