@@ -13,15 +13,16 @@
 //
 //   prep:   per sequence, its shared length P_s (whole pages before its new tokens), the suffix
 //           block-table row and suffix context length (extra workgroups of the prefix launch).
-//   prefix: one wave per (group, kv head, page chunk, row tile); rows = the group's members x new
-//           tokens x the G query heads of the kv head.  Row tiles of one chunk are adjacent waves of
-//           one workgroup, so the chunk's pages are fetched from HBM once and served from cache to
-//           the other tiles.  Each wave leaves an fp32 partial row and its log2 LSE.
+//   prefix: one wave per (group, kv head, page chunk, 32-row tile); rows = the group's members x new
+//           tokens x the G query heads of the kv head.  Over bf16 pools the four waves of a
+//           workgroup are four row tiles of one chunk and read its pages from LDS, staged once
+//           (lds_pages.h); over E4M3 pools each wave streams and widens its pages itself.  Each wave
+//           leaves an fp32 partial row and its log2 LSE.
 //   merge:  per (sequence, new token, head): the suffix result (already in out, with a natural-log
 //           LSE) merged with the row's prefix chunks.
 #include "decode_args.h"
 #include "device_common.h"
-#include "mfma_wave.h"
+#include "lds_pages.h"
 
 namespace pkv {
 
@@ -71,40 +72,17 @@ __device__ __forceinline__ void prefix_prep(const DecodeArgs &a, const PrefixArg
   }
 }
 
-// Workgroups [0, item_wgs) run the shared pass; the ones after them build the suffix tables.
-template <int D, int NBUF, bool F8>
-__global__ __launch_bounds__(256) void prefix_attend_kernel(DecodeArgs a, PrefixArgs p, int item_wgs) {
-  constexpr int NT = kPrefixRows / 16;
-  const int lane = threadIdx.x & 63;
-  if ((int)blockIdx.x >= item_wgs) {
-    prefix_prep(a, p, ((int)blockIdx.x - item_wgs) * 4 + (threadIdx.x >> 6), lane);
-    return;
-  }
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int RT = p.row_tiles;
-  const int C = p.chunks;
-  const int KVH = a.num_kv_heads;
-  if (item >= (int64_t)p.num_groups * KVH * C * RT) return;
-  // item = ((g * KVH + kvh) * C + c) * RT + rt: the row tiles of one chunk are neighbours
-  const int rt = (int)(item % RT);
-  const int c = (int)((item / RT) % C);
-  const int kvh = (int)((item / ((int64_t)RT * C)) % KVH);
-  const int g = (int)(item / ((int64_t)RT * C * KVH));
-  const int S = a.num_seqs;
-  const int gs = min(max(p.group_starts[g], 0), S);
-  const int ge = min(max(p.group_starts[g + 1], gs), S);
-  const int members = min(ge - gs, p.max_group_size);
-  const int pg = prefix_tokens(p, g);
-  const int jb = c * p.chunk_pages;
-  const int je = min(jb + p.chunk_pages, pg / kBlock);
-  if (members <= 0 || jb >= je) return;
-
+// The rows of row tile rt (32 rows) of group g for kv head kvh: member m, new token i, head offset
+// hg in member-major order; a row sees prefix keys < P_s.  Returns the fewest and the most visible
+// keys minus one over the tile's live rows (INT_MAX / -1 when it has none).
+template <int D, int NT>
+__device__ __forceinline__ void prefix_rows(const DecodeArgs &a, const PrefixArgs &p, int gs, int members, int pg,
+                                            int kvh, int rt, int col, int grp, WaveRows<D, NT> &w, int &lowest,
+                                            int &highest) {
   const int G = a.group;
   const int Qm = a.max_q_len;
-  WaveRows<D, NT> w;
-  int lowest = 0x7fffffff;
+  lowest = 0x7fffffff;
+  highest = -1;
   #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int gr = rt * kPrefixRows + n * 16 + col;
@@ -128,26 +106,119 @@ __global__ __launch_bounds__(256) void prefix_attend_kernel(DecodeArgs a, Prefix
       const uint4 v = last >= 0 ? ld16(qp + (4 * k + grp) * 16) : make_uint4(0, 0, 0, 0);
       w.qB[n][k] = __builtin_bit_cast(bf16x8_t, v);
     }
-    if (last >= 0) lowest = min(lowest, last);
+    if (last >= 0) {
+      lowest = min(lowest, last);
+      highest = max(highest, last);
+    }
   }
-  // the fewest visible keys among this wave's rows (pages below it need no mask)
-  for (int o = 1; o < 64; o <<= 1) lowest = min(lowest, __shfl_xor(lowest, o));
-  if (lowest == 0x7fffffff) return;   // no live row in this tile
+  for (int o = 1; o < 64; o <<= 1) {
+    lowest = min(lowest, __shfl_xor(lowest, o));
+    highest = max(highest, __shfl_xor(highest, o));
+  }
   w.first_last = lowest;
+}
 
-  SeqInfo si;          // the prefix as one sequence of pg tokens: every page in it is full
+// The prefix as one sequence of pg tokens (every page in it is full).
+__device__ __forceinline__ SeqInfo prefix_seq(int pg) {
+  SeqInfo si;
   si.ctx = pg;
   si.qs = 1;
   si.qbase = 0;
   si.nparts = 1;
+  return si;
+}
+
+// bf16 pools.  Workgroups [0, item_wgs) run the shared pass, one per (group, kv head, chunk, block of
+// four row tiles): the chunk's pages go through LDS once for the four waves (lds_pages.h).  The
+// workgroups after them build the suffix tables.
+template <int D>
+__global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, PrefixArgs p, int item_wgs) {
+  constexpr int NT = kPrefixRows / 16;
+  constexpr int SP = 4;
+  __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x >= item_wgs) {
+    prefix_prep(a, p, ((int)blockIdx.x - item_wgs) * 4 + wave, lane);
+    return;
+  }
+  const int RT = p.row_tiles;
+  const int RB = (RT + 3) / 4;
+  const int C = p.chunks;
+  const int KVH = a.num_kv_heads;
+  // workgroup = ((g * KVH + kvh) * C + c) * RB + rb: the row blocks of one chunk are neighbours
+  const int wi = blockIdx.x;
+  const int rb = wi % RB;
+  const int c = (wi / RB) % C;
+  const int kvh = (wi / (RB * C)) % KVH;
+  const int g = wi / (RB * C * KVH);
+  const int S = a.num_seqs;
+  const int gs = min(max(p.group_starts[g], 0), S);
+  const int ge = min(max(p.group_starts[g + 1], gs), S);
+  const int members = min(ge - gs, p.max_group_size);
+  const int pg = prefix_tokens(p, g);
+  const int jb = c * p.chunk_pages;
+  const int je = min(jb + p.chunk_pages, pg / kBlock);
+  if (members <= 0 || jb >= je) return;   // the whole workgroup
+
+  const int rt = rb * 4 + wave;
+  WaveRows<D, NT> w;
+  int lowest = 0x7fffffff, highest = -1;
+  if (rt < RT) prefix_rows<D, NT>(a, p, gs, members, pg, kvh, rt, lane & 15, lane >> 4, w, lowest, highest);
+  const bool live = highest >= 0;
+  // this wave's pages: up to its rows' last visible key
+  const int jw = live ? min(je, highest / kBlock + 1) : jb;
   WaveAcc<D, NT> st;
   init_acc<D, NT>(st);
   const int32_t *bt_row = p.prefix_blocks + (int64_t)g * (p.max_prefix_len / kBlock);
   DecodeArgs ap = a;
   ap.part_o = p.pre_o;
   ap.part_lse = p.pre_lse;
-  stream_pages<D, NT, NBUF, F8>(
-      ap, si, kvh, bt_row, jb, je, 1 << 30, lane, w, st,
+  lds_stream_pages<D, NT, SP>(ap, prefix_seq(pg), kvh, bt_row, jb, je, jw, lds, w, st);
+  const int64_t item = (((int64_t)g * KVH + kvh) * C + c) * RT + rt;
+  if (live) finish_wave<D, NT>(ap, 0, false, lane, w, st, item * kPrefixRows);
+}
+
+// E4M3 pools: one wave per (group, kv head, chunk, row tile), pages widened in registers.
+template <int D, int NBUF>
+__global__ __launch_bounds__(256) void prefix_attend_f8_kernel(DecodeArgs a, PrefixArgs p, int item_wgs) {
+  constexpr int NT = kPrefixRows / 16;
+  const int lane = threadIdx.x & 63;
+  if ((int)blockIdx.x >= item_wgs) {
+    prefix_prep(a, p, ((int)blockIdx.x - item_wgs) * 4 + (threadIdx.x >> 6), lane);
+    return;
+  }
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int RT = p.row_tiles;
+  const int C = p.chunks;
+  const int KVH = a.num_kv_heads;
+  if (item >= (int64_t)p.num_groups * KVH * C * RT) return;
+  // item = ((g * KVH + kvh) * C + c) * RT + rt: the row tiles of one chunk are neighbours
+  const int rt = (int)(item % RT);
+  const int c = (int)((item / RT) % C);
+  const int kvh = (int)((item / ((int64_t)RT * C)) % KVH);
+  const int g = (int)(item / ((int64_t)RT * C * KVH));
+  const int S = a.num_seqs;
+  const int gs = min(max(p.group_starts[g], 0), S);
+  const int ge = min(max(p.group_starts[g + 1], gs), S);
+  const int members = min(ge - gs, p.max_group_size);
+  const int pg = prefix_tokens(p, g);
+  const int jb = c * p.chunk_pages;
+  const int je = min(jb + p.chunk_pages, pg / kBlock);
+  if (members <= 0 || jb >= je) return;
+
+  WaveRows<D, NT> w;
+  int lowest, highest;
+  prefix_rows<D, NT>(a, p, gs, members, pg, kvh, rt, lane & 15, lane >> 4, w, lowest, highest);
+  if (highest < 0) return;   // no live row in this tile
+  WaveAcc<D, NT> st;
+  init_acc<D, NT>(st);
+  const int32_t *bt_row = p.prefix_blocks + (int64_t)g * (p.max_prefix_len / kBlock);
+  DecodeArgs ap = a;
+  ap.part_o = p.pre_o;
+  ap.part_lse = p.pre_lse;
+  stream_pages<D, NT, NBUF, true>(
+      ap, prefix_seq(pg), kvh, bt_row, jb, je, 1 << 30, lane, w, st,
       [&](int, int, int) { finish_wave<D, NT>(ap, 0, false, lane, w, st, item * kPrefixRows); },
       [&](int, uint4 *, uint2 *) {});
 }
@@ -221,15 +292,16 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(DecodeArgs a, PrefixA
 }
 
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st) {
-  const int64_t items = p.chunks > 0 ? (int64_t)p.num_groups * a.num_kv_heads * p.chunks * p.row_tiles : 0;
-  const int item_wgs = (int)((items + 3) / 4);
+  const int64_t tiles = p.chunks > 0 ? (int64_t)p.num_groups * a.num_kv_heads * p.chunks : 0;
+  // bf16: a workgroup per four row tiles; E4M3: a wave per row tile
+  const int item_wgs = (int)(f8 ? (tiles * p.row_tiles + 3) / 4 : tiles * ((p.row_tiles + 3) / 4));
   const dim3 grid((unsigned)(item_wgs + (a.num_seqs + 3) / 4));
   if (head_dim == 64) {
-    if (f8) prefix_attend_kernel<64, 2, true><<<grid, 256, 0, st>>>(a, p, item_wgs);
-    else prefix_attend_kernel<64, 2, false><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    if (f8) prefix_attend_f8_kernel<64, 2><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    else prefix_attend_lds_kernel<64><<<grid, 256, 0, st>>>(a, p, item_wgs);
   } else {
-    if (f8) prefix_attend_kernel<128, 2, true><<<grid, 256, 0, st>>>(a, p, item_wgs);
-    else prefix_attend_kernel<128, 2, false><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    if (f8) prefix_attend_f8_kernel<128, 2><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    else prefix_attend_lds_kernel<128><<<grid, 256, 0, st>>>(a, p, item_wgs);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,120 @@
+// K/V pages streamed through LDS for a whole workgroup: the four waves of a 256-thread workgroup each
+// own different query rows of one kv head and read the same pages, so every page is fetched from
+// HBM once per workgroup instead of once per wave.  SP pages make a stage; two stages alternate, so
+// the next stage's loads are in flight while this one is computed.  Each wave then runs the
+// decode's matrix-core page step (mfma_wave.h) on the staged pages.
+//
+// LDS layout of a page: K rows of D bf16 (one per token), each followed by PKV_LDS_KPAD bytes; V as
+// D rows of 16 tokens, each row's four 4-token groups stored in slots g ^ vswz(d) so that the dims
+// one read instruction pairs up (d and d + 8) sit in different banks.
+#pragma once
+
+#include "mfma_wave.h"
+
+#ifndef PKV_LDS_KPAD
+#define PKV_LDS_KPAD 16   // bytes after each token row of a K page (a multiple of 16)
+#endif
+
+namespace pkv {
+
+__device__ __forceinline__ int vswz(int d) { return (d >> 3) & 3; }
+
+template <int D, int SP>
+struct LdsPages {
+  static constexpr int ROWB = D * 2;
+  static constexpr int KPAD = ROWB + PKV_LDS_KPAD;   // LDS row stride of a K page
+  static constexpr int KBYTES = kBlock * KPAD;
+  static constexpr int VROW = kBlock * 2;            // LDS stride of a V dim row (16 tokens)
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int PBYTES = KBYTES + VBYTES;
+  static constexpr int CH = ROWB / 16;               // 16-byte chunks per K row
+  static constexpr int BYTES = 2 * SP * PBYTES;
+};
+
+// Logical pages [jb, je) of block-table row bt (kv head kvh) through LDS buffer `lds`
+// (LdsPages<D, SP>::BYTES).  Every thread of the workgroup must call it (it holds barriers); this
+// wave computes the pages j < jw with its rows (jw <= je; a wave with no rows passes jw = jb).
+template <int D, int NT, int SP>
+__device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
+                                                 const int32_t *bt, int jb, int je, int jw, char *lds,
+                                                 const WaveRows<D, NT> &w, WaveAcc<D, NT> &st) {
+  typedef LdsPages<D, SP> L;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int n = je - jb;
+  if (n <= 0) return;
+  const int nstages = (n + SP - 1) / SP;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  const int64_t page_bytes = (int64_t)kBlock * L::ROWB;
+  // each thread moves one 16-byte chunk of every K page and one of every V page (D = 64: threads < 128)
+  const bool mover = tid < kBlock * L::CH;
+  uint4 kn[SP], vn[SP];
+  int okn = 0;                               // bit p: page p of the stage has a valid id
+  auto fetch = [&](int stage) {
+    okn = 0;
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = jb + min(stage * SP + p, n - 1);   // past the end: re-read the last page
+      const int bid = bt[j];
+      const bool ok = bid >= 0 && bid < a.num_blocks;
+      okn |= ok ? 1 << p : 0;
+      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * 16;
+      if (mover) {
+        kn[p] = ld16(kbase + off);
+        vn[p] = ld16(vbase + off);
+      }
+    }
+  };
+  auto stage_to = [&](int b) {
+    if (mover) {
+      #pragma unroll
+      for (int p = 0; p < SP; ++p) {
+        char *pg = lds + (b * SP + p) * L::PBYTES;
+        *reinterpret_cast<uint4 *>(pg + (tid / L::CH) * L::KPAD + (tid % L::CH) * 16) = kn[p];
+        const int d = tid >> 1;
+        const int g0 = ((tid & 1) * 2) ^ vswz(d);
+        char *vrow = pg + L::KBYTES + d * L::VROW;
+        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(vn[p].x, vn[p].y);
+        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(vn[p].z, vn[p].w);
+      }
+    }
+  };
+
+  fetch(0);
+  stage_to(0);
+  int ok_cur = __builtin_amdgcn_readfirstlane(okn);
+  __syncthreads();
+  for (int g = 0; g < nstages; ++g) {
+    const int b = g & 1;
+    if (g + 1 < nstages) fetch(g + 1);
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = jb + g * SP + p;
+      if (j < jw) {
+        const char *pg = lds + (b * SP + p) * L::PBYTES;
+        uint4 kr[NK];
+        uint2 vr[ND];
+        const char *kl = pg + col * L::KPAD + grp * 16;
+        #pragma unroll
+        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
+        const char *vl = pg + L::KBYTES + col * L::VROW;
+        #pragma unroll
+        for (int t = 0; t < ND; ++t)
+          vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * L::VROW + (grp ^ vswz(col + 16 * t)) * 8);
+        mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
+      }
+    }
+    if (g + 1 < nstages) {
+      stage_to(b ^ 1);
+      ok_cur = __builtin_amdgcn_readfirstlane(okn);
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pkv

@@ -459,12 +459,19 @@ PrefixPlan make_prefix_plan(int num_seqs, int total_q, int max_q_len, int max_co
   const int pages = max_prefix_len / kBlockSize;
   const int64_t base = (int64_t)groups * num_kv_heads * pp.row_tiles;
   int chunks = 1;
-  if (base > 0 && pages > 0) {
+  if (base > 0 && pages > 0 && dtype == PKV_BF16_FP8KV) {
     const int64_t want = ceil_div(4LL * cu_count(), base);
     const int most = pages / (4 * pp.row_tiles) > 1 ? pages / (4 * pp.row_tiles) : 1;
     chunks = (int)(want < 1 ? 1 : (want > most ? most : want));
-    if (chunks > 64) chunks = 64;
+  } else if (base > 0 && pages > 0) {
+    // bf16: a workgroup per (chunk, four row tiles); about two workgroups per CU, chunks of at least
+    // one 4-page LDS stage
+    const int64_t wgs = (int64_t)groups * num_kv_heads * ceil_div(pp.row_tiles, 4);
+    const int64_t want = ceil_div(2LL * cu_count(), wgs);
+    const int most = pages / 4 > 1 ? pages / 4 : 1;
+    chunks = (int)(want < 1 ? 1 : (want > most ? most : want));
   }
+  if (chunks > 64) chunks = 64;
   pp.chunk_pages = pages > 0 ? ceil_div(pages, chunks) : 1;
   pp.chunks = pages > 0 ? ceil_div(pages, pp.chunk_pages) : 0;
   pp.items = base * pp.chunks;

@@ -19,36 +19,18 @@
 //    rows end with their final output and natural-log LSE (no split: there are enough workgroups).
 // Work units are laid out row block fastest and spread over the XCDs in contiguous ranges, so the
 // workgroups that read one (sequence, kv head)'s pages share an L2.
-#include "mfma_wave.h"
+#include "lds_pages.h"
 
 namespace pkv {
 
-#ifndef PKV_PREFILL_KPAD
-#define PKV_PREFILL_KPAD 16   // bytes after each token row of a K page in LDS (a multiple of 16)
-#endif
-#ifndef PKV_PREFILL_VPAD
-#define PKV_PREFILL_VPAD 0    // bytes after each dim row (16 tokens) of a V page in LDS (a multiple of 16)
-#endif
 constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
-
-__device__ __forceinline__ int vswz(int d) { return (d >> 3) & 3; }
 constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
 template <int D, int SP>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   constexpr int NT = kPrefillNT;
   constexpr int WROWS = 16 * NT;             // rows per wave
-  constexpr int ROWB = D * 2;
-  constexpr int KPAD = ROWB + PKV_PREFILL_KPAD;          // LDS row stride of a K page
-  constexpr int KBYTES = kBlock * KPAD;
-  constexpr int VROW = kBlock * 2 + PKV_PREFILL_VPAD;    // LDS stride of a V dim row (16 tokens)
-  constexpr int VBYTES = D * VROW;                       // V page [D][16]
-  constexpr int PBYTES = KBYTES + VBYTES;
-  constexpr int NK = D / 32;
-  constexpr int ND = D / 16;
-  constexpr int CH = ROWB / 16;              // 16-byte chunks per K row
-  // two stages of SP pages: the next stage's loads fly while this stage is computed
-  __shared__ __attribute__((aligned(16))) char lds[2][SP][PBYTES];
+  __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -83,7 +65,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   const int wg_last_tok = (min(rows, wg_row0 + kPrefillRows) - 1) / G;
   const int npages = (si.ctx - si.qs + wg_last_tok) / kBlock + 1;
   const int my_pages = row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + WROWS) - 1) / G) / kBlock + 1 : 0;
-  const int nstages = (npages + SP - 1) / SP;
 
   WaveRows<D, NT> w;
   load_rows<D, NT>(a, si, kvh, row0, rows, col, grp, w);
@@ -91,73 +72,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   init_acc<D, NT>(st);
 
   const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const char *kbase = static_cast<const char *>(a.k_cache);
-  const char *vbase = static_cast<const char *>(a.v_cache);
-  const int64_t page_bytes = (int64_t)kBlock * ROWB;
-  // each thread moves one 16-byte chunk of every K page and one of every V page (D = 64: threads < 128)
-  const bool mover = tid < kBlock * CH;
-  uint4 kn[SP], vn[SP];
-  int okn = 0;                               // bit p: page p of the stage has a valid id
-  auto fetch = [&](int stage) {
-    okn = 0;
-    #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      const int j = min(stage * SP + p, npages - 1);   // past the end: re-read the last page
-      const int bid = bt[j];
-      const bool ok = bid >= 0 && bid < a.num_blocks;
-      okn |= ok ? 1 << p : 0;
-      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * 16;
-      if (mover) {
-        kn[p] = ld16(kbase + off);
-        vn[p] = ld16(vbase + off);
-      }
-    }
-  };
-  auto stage_to = [&](int b) {
-    if (mover) {
-      #pragma unroll
-      for (int p = 0; p < SP; ++p) {
-        *reinterpret_cast<uint4 *>(&lds[b][p][(tid / CH) * KPAD + (tid % CH) * 16]) = kn[p];
-        // V dim row d keeps its four 4-token groups in slots g ^ vswz(d): the dims a read instruction
-        // pairs up (d and d + 8) then sit in different banks
-        const int d = tid >> 1;
-        const int g0 = ((tid & 1) * 2) ^ vswz(d);
-        char *vrow = &lds[b][p][KBYTES + d * VROW];
-        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(vn[p].x, vn[p].y);
-        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(vn[p].z, vn[p].w);
-      }
-    }
-  };
-
-  fetch(0);
-  stage_to(0);
-  int ok_cur = __builtin_amdgcn_readfirstlane(okn);
-  __syncthreads();
-  for (int g = 0; g < nstages; ++g) {
-    const int b = g & 1;
-    if (g + 1 < nstages) fetch(g + 1);
-    #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      const int j = g * SP + p;
-      if (j < my_pages) {
-        uint4 kr[NK];
-        uint2 vr[ND];
-        const char *kl = &lds[b][p][col * KPAD + grp * 16];
-        #pragma unroll
-        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
-        const char *vl = &lds[b][p][KBYTES + col * VROW];
-        #pragma unroll
-        for (int t = 0; t < ND; ++t)
-          vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * VROW + (grp ^ vswz(col + 16 * t)) * 8);
-        mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
-      }
-    }
-    if (g + 1 < nstages) {
-      stage_to(b ^ 1);
-      ok_cur = __builtin_amdgcn_readfirstlane(okn);
-    }
-    __syncthreads();
-  }
+  lds_stream_pages<D, NT, SP>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
   if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
 }
 
