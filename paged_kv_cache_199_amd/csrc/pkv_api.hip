@@ -420,7 +420,10 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
 namespace {
 
 // Read-once shared-prefix decode: workspace carving and the chunking of the prefix pass.
-constexpr int64_t kReadOnceBytes = 64ll << 20;
+// Bytes the read-once pass must save before it pays: measured crossover over groups of 4..64
+// sequences sharing 512..4096 tokens (GQA 4, D 128) lies between 250 and 500 MiB, because the
+// per-sequence decode reads the shared pages from the Infinity Cache after the first sequence.
+constexpr int64_t kReadOnceBytes = 448ll << 20;
 struct PrefixPlan {
   int rows_max, row_tiles, chunk_pages, chunks, sfx_stride;
   int64_t items;
@@ -539,9 +542,9 @@ int pkv_paged_attn_decode_shared_prefix(const void *q, const void *k_cache, cons
   const PrefixPlan pp = make_prefix_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                                          head_dim, dtype, num_groups, max_group_size, max_prefix_len, opts);
   if (!workspace || workspace_bytes < pp.bytes) return PKV_ERR_WORKSPACE;
-  // Policy: the shared pass costs two launches more than the per-sequence decode (about 10 us); it
-  // pays when the K/V bytes it saves (every member past the first reading the whole prefix) take
-  // longer than that to stream.
+  // Policy: the shared pass costs two launches more than the per-sequence decode (8 us or more); it
+  // pays when the K/V bytes it saves (every member past the first reading the whole prefix) are
+  // large enough that even their cache-served reads take longer than that.
   const int mode = opts ? opts->shared_prefix_mode : PKV_PREFIX_AUTO;
   const int64_t saved = (int64_t)(num_groups > 0 ? num_groups : 0) * (max_group_size > 1 ? max_group_size - 1 : 0) *
                         max_prefix_len * num_kv_heads * head_dim * 2 * (dtype == PKV_BF16_FP8KV ? 1 : 2);
