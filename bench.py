@@ -499,8 +499,7 @@ def main():
 
     ev = [(new_event(), new_event()) for _ in range(args.steps)]
 
-    # E4M3 pools append through the quantizing slot-mapped write (the fused append is bf16 only)
-    append_mode = "slots" if spec.kv_fp8 else args.append
+    append_mode = args.append
     dstep = _lib.DecodeStep(w.q, kcs[0], vcs[0], meta["block_tables"], meta["context_lens"], q_lens, out, lse,
                             H, KVH, D, spec.block_size, w.scale, w.max_context_len, max_q_len=w.max_q_len,
                             partition_size=P, path=path, depth=args.depth, schedule=sched, workspace=ws,

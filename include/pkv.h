@@ -196,7 +196,10 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
  * the slot_mapping a caller of pkv_kv_cache_write would pass).  The result equals
  * pkv_kv_cache_write with those slots followed by pkv_paged_attn_decode, bit for bit.  The matrix-core
  * persistent schedule does both in one pass for up to 8 new tokens per sequence; other launches run
- * a small append kernel first.  Extra precondition: no other sequence of the batch reads the new
+ * a small append kernel first.  PKV_BF16_FP8KV: new_k / new_v are bf16 and are stored as E4M3 codes
+ * (quantized as pkv_kv_cache_write_fp8 does, with the options' scales); the result equals
+ * pkv_kv_cache_write_fp8 followed by pkv_paged_attn_decode, bit for bit; up to 8 new tokens per
+ * sequence (PKV_ERR_UNSUPPORTED above).  Extra precondition: no other sequence of the batch reads the new
  * tokens' slots (a block shared by several sequences is copied before it is appended to).  Other
  * arguments, preconditions and errors as pkv_paged_attn_decode; new_k / new_v NULL -> PKV_ERR_NULL.
  */

@@ -19,13 +19,15 @@ extern "C" {
  * K page page_index[j] and V page page_index[j] for j in [wave_offsets[w], wave_offsets[w + 1]),
  * keeping a ring of 3 pages in flight, exactly as the matrix-core decode kernel loads a 16-token
  * page of one kv head.  Page p starts at k_pool + p * page_bytes (and v_pool + p * page_bytes);
- * page_bytes = 16 * head_dim * 2 (bf16), so head_dim is 64 or 128.  Indexes outside
- * [0, pool_pages) are read as page 0.  A value derived from the data goes to *sink so the loads are
- * not optimised away.  Device pointers; enqueued on `stream`; returns 0 or a negative pkv_status.
+ * page_bytes = 16 * head_dim * elem_bytes: elem_bytes 2 for bf16 pools, 1 for E4M3 pools (loaded
+ * with the decode kernel's E4M3 shapes); head_dim is 64 or 128.  Each pool must hold pool_pages
+ * pages.  Indexes outside [0, pool_pages) are read as page 0.  A value derived from the data goes to
+ * *sink so the loads are not optimised away.  Device pointers; enqueued on `stream`; returns 0 or a
+ * negative pkv_status (PKV_ERR_UNSUPPORTED for another head_dim or elem_bytes).
  */
 int pkv_probe_page_stream(const void *k_pool, const void *v_pool, int64_t pool_pages, int head_dim,
-                          const int32_t *page_index, const int32_t *wave_offsets, int num_waves,
-                          uint32_t *sink, void *stream);
+                          int elem_bytes, const int32_t *page_index, const int32_t *wave_offsets,
+                          int num_waves, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,7 @@ EXPORTS = {
                                               ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
     "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
                                         _vp]),
-    "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _vp, _vp, _c_int, _vp, _vp]),
+    "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp]),
     "pkv_decode_shared_prefix_workspace_bytes": (_c_sz, [_c_int] * 11 + [ctypes.POINTER(DecodeOptions)]),
     "pkv_paged_attn_decode_shared_prefix": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
@@ -222,8 +222,11 @@ def probe_page_stream(k_cache: torch.Tensor, v_cache: torch.Tensor, page_index: 
     lib = load()
     nb, kvh, B, D = k_cache.shape
     _need(page_index.dtype == torch.int32 and wave_offsets.dtype == torch.int32, "int32 lists")
-    rc = lib.pkv_probe_page_stream(_ptr(k_cache), _ptr(v_cache), nb * kvh, D, _ptr(page_index),
-                                   _ptr(wave_offsets), wave_offsets.numel() - 1, _ptr(sink), _stream(stream))
+    _need(k_cache.dtype in (torch.bfloat16, torch.uint8) and v_cache.dtype == k_cache.dtype
+          and v_cache.numel() == k_cache.numel() and B == BLOCK_SIZE, "bf16 or uint8 (E4M3) pools of one shape")
+    rc = lib.pkv_probe_page_stream(_ptr(k_cache), _ptr(v_cache), nb * kvh, D, k_cache.element_size(),
+                                   _ptr(page_index), _ptr(wave_offsets), wave_offsets.numel() - 1, _ptr(sink),
+                                   _stream(stream))
     _check(rc, "pkv_probe_page_stream")
 
 

@@ -29,6 +29,7 @@ struct DecodeArgs {
   int group;                   // num_heads / num_kv_heads
   float scale_log2;            // scale * log2(e) (* the K pool's scale): scores live in log2 units
   float v_scale;               // the V pool's scale (1 for bf16 pools)
+  float k_scale;               // the K pool's scale (1 for bf16 pools; scale_log2 already holds it)
   int part_size;               // keys per partition
   int num_parts;               // ceil(max_context_len / part_size)
   int row_tiles;               // row tiles per (sequence, kv head)

@@ -134,7 +134,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 template <int D, int NT, int NBUF, bool APPEND, bool F8>
 __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs a) {
   constexpr int ROWS = 16 * NT;
-  constexpr int APP = 2 * AppendRows<D>::MAXQ * AppendRows<D>::CH;   // staging chunks per wave
+  constexpr int APP = 2 * AppendRows<D, F8>::MAXQ * AppendRows<D, F8>::CH;   // staging chunks per wave
   __shared__ uint4 app_lds[APPEND ? 4 : 1][APPEND ? APP : 1];
   extern __shared__ int sh[];
   const int S = a.num_seqs;
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // appending: does this run reach the new tokens (the sequence's last qs positions)?
     const bool reach = APPEND && (j0 + run) * kBlock > si.ctx - si.qs;
-    AppendRows<D> ar;
-    if (reach) append_load<D>(a, si, kvh, lane, ar);
+    AppendRows<D, F8> ar;
+    if (reach) append_load<D, F8>(a, si, kvh, lane, ar);
     WaveRows<D, NT> w;
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
     WaveAcc<D, NT> st;
@@ -252,10 +252,10 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
         },
         [&](int j, uint4 *kr, uint2 *vr) {
           if constexpr (APPEND) {
-            if (reach) append_patch<D>(j, lane, ar, app_lds[wave], kr, vr);
+            if (reach) append_patch<D, F8>(j, lane, ar, app_lds[wave], kr, vr);
           }
         });
-    if (reach && rt == 0) append_store<D>(a, kvh, bt_row, j0, j0 + run, lane, ar);
+    if (reach && rt == 0) append_store<D, F8>(a, kvh, bt_row, j0, j0 + run, lane, ar);
     k += run;
   }
 }
@@ -280,12 +280,13 @@ static void launch_persistent(const DecodeArgs &a, int depth, int grid, hipStrea
   else decode_mfma_persistent_kernel<D, NT, 4, APPEND, F8><<<grid, 256, lds, st>>>(a);
 }
 
-// f8: E4M3 pools (persistent schedule only, no fused append).
+// f8: E4M3 pools (persistent schedule only).
 template <int D, int NT>
 static hipError_t launch_mfma_dn(const DecodeArgs &a, int depth, bool persistent, int grid, bool f8,
                                  hipStream_t st) {
   if (persistent) {
-    if (f8) launch_persistent<D, NT, false, true>(a, depth, grid, st);
+    if (f8 && a.new_k) launch_persistent<D, NT, true, true>(a, depth, grid, st);
+    else if (f8) launch_persistent<D, NT, false, true>(a, depth, grid, st);
     else if (a.new_k) launch_persistent<D, NT, true, false>(a, depth, grid, st);
     else launch_persistent<D, NT, false, false>(a, depth, grid, st);
     return hipGetLastError();

@@ -18,6 +18,7 @@
 
 #include "decode_args.h"
 #include "device_common.h"
+#include "e4m3.h"
 
 namespace pkv {
 
@@ -344,46 +345,70 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
 // pages); on each page that holds new tokens it stages them through its LDS area and substitutes
 // them for the cache rows it just loaded (so no other wave's write has to come first); after the
 // run, row tile 0 stores them into their cache slots.  The K/V row of token i is row qbase + i of
-// new_k / new_v [total_q, KVH, D].
-template <int D>
+// new_k / new_v [total_q, KVH, D] (bf16).  Over E4M3 pools (F8) the rows are quantized once when
+// loaded, exactly as the slot-mapped write does it (x / scale in fp32, nearest code): the codes are
+// what gets stored, and what the page walk substitutes is their exact bf16 value, the same value a
+// separate write followed by decode would read back.
+template <int D, bool F8 = false>
 struct AppendRows {
   static constexpr int ROWB = D * 2;
-  static constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  static constexpr int CH = ROWB / 16;                    // 16-byte chunks per bf16 row
   static constexpr int MAXQ = 8;                          // new tokens per sequence on this path
   static constexpr int PER_LANE = (MAXQ * CH + 63) / 64;
-  uint4 k[PER_LANE];
+  uint4 k[PER_LANE];                                      // bf16 (F8: the codes' exact values)
   uint4 v[PER_LANE];
+  uint2 kq[F8 ? PER_LANE : 1];                            // F8: the 8 codes of each chunk
+  uint2 vq[F8 ? PER_LANE : 1];
   int first;       // position of new token 0
   int n;           // new tokens
   bool staged;
 };
 
-template <int D>
+// 8 bf16 (one 16-byte chunk) -> their 8 E4M3 codes under `scale`, and the codes' exact bf16 values.
+__device__ __forceinline__ void quantize_chunk(const uint4 &x, float scale, uint2 &codes, uint4 &back) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t c[2] = {0u, 0u};
+  #pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    c[e >> 2] |= e4m3_code(__uint_as_float(h << 16) / scale) << (8 * (e & 3));
+  }
+  codes = make_uint2(c[0], c[1]);
+  back = make_uint4(fp8x2_to_bf16x2<false>(c[0]), fp8x2_to_bf16x2<true>(c[0]), fp8x2_to_bf16x2<false>(c[1]),
+                    fp8x2_to_bf16x2<true>(c[1]));
+}
+
+template <int D, bool F8>
 __device__ __forceinline__ void append_load(const DecodeArgs &a, const SeqInfo &si, int kvh, int lane,
-                                            AppendRows<D> &r) {
-  constexpr int CH = AppendRows<D>::CH;
+                                            AppendRows<D, F8> &r) {
+  constexpr int CH = AppendRows<D, F8>::CH;
   r.first = si.ctx - si.qs;
-  r.n = min(si.qs, AppendRows<D>::MAXQ);   // more new tokens than that is a broken precondition
+  r.n = min(si.qs, AppendRows<D, F8>::MAXQ);   // more new tokens than that is a broken precondition
   r.staged = false;
   const char *nk = static_cast<const char *>(a.new_k);
   const char *nv = static_cast<const char *>(a.new_v);
   #pragma unroll
-  for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+  for (int u = 0; u < AppendRows<D, F8>::PER_LANE; ++u) {
     const int c = lane + 64 * u;
     const int tok = c / CH;
     const bool ok = tok < r.n && si.qbase + tok < a.total_q;
     const int64_t off = (((int64_t)(ok ? si.qbase + tok : 0) * a.num_kv_heads + kvh) * CH + c % CH) * 16;
     r.k[u] = ok ? ld16(nk + off) : make_uint4(0, 0, 0, 0);
     r.v[u] = ok ? ld16(nv + off) : make_uint4(0, 0, 0, 0);
+    if constexpr (F8) {
+      quantize_chunk(r.k[u], a.k_scale, r.kq[u], r.k[u]);
+      quantize_chunk(r.v[u], a.v_scale, r.vq[u], r.v[u]);
+    }
   }
 }
 
-// Page j (logical) of the run: substitute the new tokens it holds for the cache rows just loaded.
-// lds: this wave's staging area, 2 * MAXQ * CH chunks.
-template <int D>
-__device__ __forceinline__ void append_patch(int j, int lane, AppendRows<D> &r, uint4 *lds, uint4 *kr,
+// Page j (logical) of the run: substitute the new tokens it holds for the (widened) cache rows just
+// loaded.  lds: this wave's staging area, 2 * MAXQ * CH chunks.
+template <int D, bool F8>
+__device__ __forceinline__ void append_patch(int j, int lane, AppendRows<D, F8> &r, uint4 *lds, uint4 *kr,
                                              uint2 *vr) {
-  constexpr int CH = AppendRows<D>::CH;
+  constexpr int CH = AppendRows<D, F8>::CH;
+  constexpr int MAXQ = AppendRows<D, F8>::MAXQ;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   const int p0 = j * kBlock;
@@ -392,17 +417,17 @@ __device__ __forceinline__ void append_patch(int j, int lane, AppendRows<D> &r, 
   const int grp = lane >> 4;
   if (!r.staged) {
     #pragma unroll
-    for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+    for (int u = 0; u < AppendRows<D, F8>::PER_LANE; ++u) {
       const int c = lane + 64 * u;
       if (c < r.n * CH) {
         lds[c] = r.k[u];
-        lds[AppendRows<D>::MAXQ * CH + c] = r.v[u];
+        lds[MAXQ * CH + c] = r.v[u];
       }
     }
     wave_lds_sync();
     r.staged = true;
   }
-  const uint16_t *lv = reinterpret_cast<const uint16_t *>(lds + AppendRows<D>::MAXQ * CH);
+  const uint16_t *lv = reinterpret_cast<const uint16_t *>(lds + MAXQ * CH);
   const int kpos = p0 + col;
   if (kpos >= r.first && kpos < r.first + r.n) {
     const int tok = kpos - r.first;
@@ -427,17 +452,17 @@ __device__ __forceinline__ void append_patch(int j, int lane, AppendRows<D> &r, 
 }
 
 // After the run: store the new tokens that live on its pages [jb, je) into their cache slots (row
-// tile 0 only, so each slot is written once).  Stores wait until the page loads are done: on this
-// chip they share the counter the page ring waits on.
-template <int D>
+// tile 0 only, so each slot is written once): bf16 rows, or (F8) their codes.  Stores wait until the
+// page loads are done: on this chip they share the counter the page ring waits on.
+template <int D, bool F8>
 __device__ __forceinline__ void append_store(const DecodeArgs &a, int kvh, const int32_t *bt_row, int jb, int je,
-                                             int lane, const AppendRows<D> &r) {
-  constexpr int CH = AppendRows<D>::CH;
-  constexpr int ROWB = AppendRows<D>::ROWB;
+                                             int lane, const AppendRows<D, F8> &r) {
+  constexpr int CH = AppendRows<D, F8>::CH;
+  constexpr int EB = F8 ? 1 : 2;                          // bytes per cache element
   char *kc = static_cast<char *>(const_cast<void *>(a.k_cache));
-  uint16_t *vc = static_cast<uint16_t *>(const_cast<void *>(a.v_cache));
+  char *vc = static_cast<char *>(const_cast<void *>(a.v_cache));
   #pragma unroll
-  for (int u = 0; u < AppendRows<D>::PER_LANE; ++u) {
+  for (int u = 0; u < AppendRows<D, F8>::PER_LANE; ++u) {
     const int c = lane + 64 * u;
     const int tok = c / CH;
     const int pos = r.first + tok;
@@ -445,13 +470,22 @@ __device__ __forceinline__ void append_store(const DecodeArgs &a, int kvh, const
     if (tok < r.n && j >= jb && j < je) {
       const int64_t bid = bt_row[j];
       if (bid >= 0 && bid < a.num_blocks) {
-        const int cc = c % CH;
+        const int cc = c % CH;                            // elements cc * 8 .. cc * 8 + 7 of the row
         const int off = pos - j * kBlock;
         const int64_t page = bid * a.num_kv_heads + kvh;
-        *reinterpret_cast<uint4 *>(kc + (page * kBlock + off) * ROWB + cc * 16) = r.k[u];
-        const uint16_t *e = reinterpret_cast<const uint16_t *>(&r.v[u]);
-        #pragma unroll
-        for (int q = 0; q < 8; ++q) vc[(page * D + cc * 8 + q) * kBlock + off] = e[q];
+        if constexpr (F8) {
+          *reinterpret_cast<uint2 *>(kc + (page * kBlock + off) * D + cc * 8) = r.kq[u];
+          const uint32_t vw[2] = {r.vq[u].x, r.vq[u].y};
+          #pragma unroll
+          for (int q = 0; q < 8; ++q)
+            vc[(page * D + cc * 8 + q) * kBlock + off] = (char)((vw[q >> 2] >> (8 * (q & 3))) & 0xffu);
+        } else {
+          *reinterpret_cast<uint4 *>(kc + (page * kBlock + off) * D * EB + cc * 16) = r.k[u];
+          const uint16_t *e = reinterpret_cast<const uint16_t *>(&r.v[u]);
+          uint16_t *v16 = reinterpret_cast<uint16_t *>(vc);
+          #pragma unroll
+          for (int q = 0; q < 8; ++q) v16[(page * D + cc * 8 + q) * kBlock + off] = e[q];
+        }
       }
     }
   }

@@ -317,8 +317,9 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.part_lse = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_lse) : nullptr;
   a.part_o = pl.part_rows > 0 ? reinterpret_cast<float *>(ws + pl.off_part_o) : nullptr;
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
-  // E4M3 pools: the matrix-core persistent schedule only, and no append in this call
-  if (f8 && (pl.path != PKV_PATH_MFMA || !persist || new_k)) return PKV_ERR_UNSUPPORTED;
+  // E4M3 pools: the matrix-core persistent schedule only; an append in the same call only where that
+  // kernel does it itself (up to 8 new tokens per sequence)
+  if (f8 && (pl.path != PKV_PATH_MFMA || !persist || (new_k && max_q_len > 8))) return PKV_ERR_UNSUPPORTED;
   a.item_pre = persist ? reinterpret_cast<int32_t *>(ws + pl.off_item_pre) : nullptr;
   a.spill_base = pl.spill_base;
   a.share_waves = pl.grid / 8 * 4;
@@ -342,10 +343,12 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.group = num_heads / num_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.v_scale = 1.f;
+  a.k_scale = 1.f;
   if (f8) {
     // the pools' scales factor out of the products: K's into the scores, V's into the epilogue
     const float ks = opts && opts->k_scale > 0.f ? opts->k_scale : 1.f;
     a.scale_log2 *= ks;
+    a.k_scale = ks;
     a.v_scale = opts && opts->v_scale > 0.f ? opts->v_scale : 1.f;
   }
   a.part_size = pl.part_size;

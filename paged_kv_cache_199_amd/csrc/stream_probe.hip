@@ -3,20 +3,26 @@
 #include "pkv.h"
 #include "pkv_probe.h"
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace pkv {
 
 typedef const __attribute__((address_space(4))) int32_t const_i32_probe;
 
-template <int D, int NBUF>
+// F8: 1-byte E4M3 pools, loaded with the decode kernel's E4M3 shapes (half the bytes per lane).
+template <int D, int NBUF, bool F8>
 __global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict__ K, const char *__restrict__ V,
                                                           int64_t pool_pages, const int32_t *__restrict__ list,
                                                           const int32_t *__restrict__ offs, int num_waves,
                                                           uint32_t *sink) {
-  constexpr int ROWB = D * 2;
+  constexpr int EB = F8 ? 1 : 2;             // bytes per cache element
+  constexpr int ROWB = D * EB;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
+  typedef typename std::conditional<F8, uint2, uint4>::type KR;      // 8 elements of a K row
+  typedef typename std::conditional<F8, uint32_t, uint2>::type VR;   // 4 tokens of a V dim
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -33,21 +39,21 @@ __global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict
     return id >= 0 && id < pool_pages ? id : 0;
   };
   uint32_t acc = 0;
-  uint4 kb[NBUF][NK];
-  uint2 vb[NBUF][ND];
-  auto issue = [&](int64_t id, uint4 *kr, uint2 *vr) {
-    const char *kp = K + id * page_bytes + col * ROWB + grp * 16;
+  KR kb[NBUF][NK];
+  VR vb[NBUF][ND];
+  auto issue = [&](int64_t id, KR *kr, VR *vr) {
+    const char *kp = K + id * page_bytes + col * ROWB + grp * 8 * EB;
     #pragma unroll
-    for (int c = 0; c < NK; ++c) kr[c] = ld16(kp + c * 64);
-    const char *vp = V + id * page_bytes + (col * kBlock + 4 * grp) * 2;
+    for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const KR *>(kp + c * 32 * EB);
+    const char *vp = V + id * page_bytes + (col * kBlock + 4 * grp) * EB;
     #pragma unroll
-    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(vp + t * 16 * kBlock * 2);
+    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
   };
-  auto use = [&](const uint4 *kr, const uint2 *vr) {
+  auto use = [&](const KR *kr, const VR *vr) {
     #pragma unroll
-    for (int c = 0; c < NK; ++c) acc += kr[c].x ^ kr[c].w;
+    for (int c = 0; c < NK; ++c) acc += kr[c].x ^ kr[c].y;
     #pragma unroll
-    for (int t = 0; t < ND; ++t) acc += vr[t].x ^ vr[t].y;
+    for (int t = 0; t < ND; ++t) acc += reinterpret_cast<const uint32_t *>(&vr[t])[0];
   };
   int64_t sid[NBUF];
   #pragma unroll
@@ -73,19 +79,23 @@ __global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict
 }  // namespace pkv
 
 extern "C" int pkv_probe_page_stream(const void *k_pool, const void *v_pool, int64_t pool_pages, int head_dim,
-                                     const int32_t *page_index, const int32_t *wave_offsets, int num_waves,
-                                     uint32_t *sink, void *stream) {
+                                     int elem_bytes, const int32_t *page_index, const int32_t *wave_offsets,
+                                     int num_waves, uint32_t *sink, void *stream) {
   if (!k_pool || !v_pool || !page_index || !wave_offsets || !sink) return PKV_ERR_NULL;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if ((head_dim != 64 && head_dim != 128) || (elem_bytes != 1 && elem_bytes != 2)) return PKV_ERR_UNSUPPORTED;
   if (num_waves < 0 || pool_pages < 1) return PKV_ERR_SHAPE;
   if (num_waves == 0) return PKV_OK;
   const int grid = (num_waves + 3) / 4;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const char *K = static_cast<const char *>(k_pool);
   const char *V = static_cast<const char *>(v_pool);
-  if (head_dim == 64)
-    pkv::page_stream_kernel<64, 3><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+  if (head_dim == 64 && elem_bytes == 2)
+    pkv::page_stream_kernel<64, 3, false><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+  else if (head_dim == 64)
+    pkv::page_stream_kernel<64, 3, true><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+  else if (elem_bytes == 2)
+    pkv::page_stream_kernel<128, 3, false><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
   else
-    pkv::page_stream_kernel<128, 3><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
+    pkv::page_stream_kernel<128, 3, true><<<grid, 256, 0, st>>>(K, V, pool_pages, page_index, wave_offsets, num_waves, sink);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }

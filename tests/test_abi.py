@@ -140,6 +140,10 @@ def test_fp8_pool_limits(lib):
     assert w(None, fake, fake, fake, fake, 4, 8, 2, 64, 16, 1.0, 1.0, None) == -1
     assert w(fake, fake, fake, fake, fake, 0, 8, 2, 64, 16, 1.0, 1.0, None) == 0
     assert lib.pkv_kv_cache_write(fake, fake, fake, fake, fake, 4, 8, 2, 64, 16, 2, None) == -3  # not via plain write
+    # the decode call appends over E4M3 pools only where the persistent kernel does it itself (<= 8 tokens)
+    app = lib.pkv_paged_attn_decode_append
+    assert app(fake, fake, fake, fake, fake, fake, fake, None, fake, None, 4, 64, 36, 9, 1024, 64, 8, 2, 128, 16,
+               0.1, 2, None, fake, 1 << 30, None) == -3
 
 
 def test_shared_prefix_argument_validation(lib):
@@ -182,9 +186,14 @@ def test_prefill_argument_validation(lib):
 
 def test_probe_argument_validation(lib):
     f = ctypes.c_void_p(0x1000)
-    assert lib.pkv_probe_page_stream(None, f, 8, 128, f, f, 4, f, None) == -1
-    assert lib.pkv_probe_page_stream(f, f, 8, 96, f, f, 4, f, None) == -3
-    assert lib.pkv_probe_page_stream(f, f, 8, 128, f, f, 0, f, None) == 0
+    assert lib.pkv_probe_page_stream(None, f, 8, 128, 2, f, f, 4, f, None) == -1
+    assert lib.pkv_probe_page_stream(f, f, 8, 96, 2, f, f, 4, f, None) == -3
+    assert lib.pkv_probe_page_stream(f, f, 8, 128, 4, f, f, 4, f, None) == -3     # bf16 or E4M3 pages only
+    assert lib.pkv_probe_page_stream(f, f, 8, 128, 1, f, f, 0, f, None) == 0
+    import torch
+    with pytest.raises(ValueError):                  # fp32 pools: the probe has no such page shape
+        _lib.probe_page_stream(torch.zeros(2, 1, 16, 64), torch.zeros(2, 1, 64, 16), torch.zeros(1, dtype=torch.int32),
+                               torch.zeros(2, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
 
 
 def test_write_argument_validation(lib):

@@ -128,3 +128,68 @@ def test_fp8_step_write_then_decode(gpu_lib):
     d_out, d_lse = compare(w, out, lse, *oracle_full(w))
     _say(f"[case] fp8 step: max|d out| {d_out:.3e} max|d lse| {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+
+
+def _fp8_append_case(spec, label, variants=({},)):
+    """Fused append over E4M3 pools: the pools must hold the oracle quantizer's codes at the new
+    tokens' slots (derived here from the block tables), the output must match the oracle over those
+    pools, and both must equal pkv_kv_cache_write_fp8 with the same slots followed by decode, bit for
+    bit."""
+    w = W.build(spec, DEV)
+    B = 16
+    slots = []
+    for s in range(w.num_seqs):
+        n, q = int(w.context_lens[s]), int(w.q_lens[s])
+        for i in range(q):
+            p = n - q + i
+            slots.append(int(w.block_tables[s, p // B]) * B + p % B)
+    slots = np.asarray(slots, dtype=np.int64)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    shape = (w.total_q, w.spec.num_kv_heads, w.spec.head_dim)
+    nk = torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+    nv = torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+    ks, vs = w.spec.k_scale, w.spec.v_scale
+    kc0, vc0 = host_bits(w.k_cache), host_bits(w.v_cache)
+    want_k, want_v = O.kv_cache_write(kc0, vc0, F.quantize(nk.float().cpu().numpy(), ks),
+                                      F.quantize(nv.float().cpu().numpy(), vs), slots)
+    meta = w.device_meta(DEV)
+    qlens = None if w.uniform_q else meta["q_lens"]
+    ref = O.paged_decode_attention(host_bits(w.q), F.dequantize(want_k, ks), F.dequantize(want_v, vs),
+                                   w.block_tables, w.context_lens, w.q_lens, w.scale, w.spec.num_kv_heads, B)
+    for kw in variants:
+        _say(f"[case] {label} fused append {kw}")
+        kc, vc = w.k_cache.clone(), w.v_cache.clone()
+        out = torch.empty_like(w.q)
+        lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=DEV)
+        _lib.paged_attn_decode(w.q, kc, vc, meta["block_tables"], meta["context_lens"], qlens, out, lse,
+                               w.spec.num_heads, w.spec.num_kv_heads, w.spec.head_dim, B, w.scale, w.max_context_len,
+                               max_q_len=w.max_q_len, new_k=nk, new_v=nv, k_scale=ks, v_scale=vs, **kw)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(kc), want_k) and np.array_equal(host_bits(vc), want_v)
+        d_out, d_lse = compare(w, out, lse, *ref)
+        _say(f"   max|d out| {d_out:.3e} max|d lse| {d_lse:.3e}")
+        assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+        kc2, vc2 = w.k_cache.clone(), w.v_cache.clone()
+        _lib.kv_cache_write_fp8(nk, nv, torch.from_numpy(slots).to(DEV), kc2, vc2, ks, vs)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        _lib.paged_attn_decode(w.q, kc2, vc2, meta["block_tables"], meta["context_lens"], qlens, out2, lse2,
+                               w.spec.num_heads, w.spec.num_kv_heads, w.spec.head_dim, B, w.scale, w.max_context_len,
+                               max_q_len=w.max_q_len, k_scale=ks, v_scale=vs, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+def test_fp8_fused_append_one_token(gpu_lib):
+    _fp8_append_case(W.named("conc32_fp8kv"), "conc32_fp8kv", ({}, dict(depth=3), dict(partition_size=128)))
+
+
+def test_fp8_fused_append_ragged_and_page_edges(gpu_lib):
+    spec = W.custom("fp8_app", [5, 17, 20, 33, 36, 100, 513, 8], q_len=[5, 2, 5, 1, 4, 3, 8, 8], num_heads=16,
+                    num_kv_heads=2, head_dim=64, kv_fp8=True)
+    _fp8_append_case(spec, "fp8 ragged q D 64")
+    spec = W.custom("fp8_app_g8", [40, 700, 18, 1025], q_len=[3, 1, 3, 2], num_heads=64, num_kv_heads=2,
+                    head_dim=128, kv_fp8=True)
+    _fp8_append_case(spec, "fp8 GQA 32 row tiles")
