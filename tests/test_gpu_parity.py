@@ -145,6 +145,25 @@ def test_balanced_split_many_short_sequences(gpu_lib):
         _check_persistent(w, 0, depth)
 
 
+@pytest.mark.parametrize("S", [4096, 4100])
+def test_largest_batch_the_persistent_schedule_lists(gpu_lib, S):
+    """4096 sequences: the persistent kernel's LDS tables at their largest (the library's limit);
+    4100: past it, the plan falls back to the grid schedule.  Short ragged contexts, fused append."""
+    rng = np.random.default_rng(S)
+    ctx = rng.integers(1, 48, S)
+    ql = np.minimum(rng.integers(1, 3, S), ctx)
+    spec = W.custom(f"batch{S}", ctx.tolist(), q_len=ql.tolist(), num_heads=8, num_kv_heads=2, head_dim=64)
+    w = W.build(spec, DEV)
+    plan = _lib.decode_plan(S, w.total_q, w.max_q_len, w.max_context_len, 8, 2, 64, _lib.PKV_BF16)
+    assert plan["schedule"] == (_lib.SCHEDULE_PERSISTENT if S <= 4096 else _lib.SCHEDULE_GRID)
+    _say(f"[case] {S} sequences, schedule {plan['schedule']}")
+    out, lse = run_library(w, DEV)
+    ref_out, ref_lse = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
+    assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+
+
 def test_balanced_split_several_row_tiles(gpu_lib):
     """96 query rows per kv head (GQA 32, 3 new tokens): three 32-row tiles, each its own work item."""
     spec = W.custom("row_tiles", [700, 40, 2000, 3], q_len=3, num_heads=64, num_kv_heads=2, head_dim=128)
