@@ -66,12 +66,15 @@ def write_bytes(w) -> int:
     return rows * w.spec.num_kv_heads * w.spec.head_dim * (e + ekv) * 2 + rows * 8
 
 
+# the sources the decode partition kernels are built from (the kernel the traffic record measures)
+DECODE_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "mfma_wave.h", "decode_args.h", "device_common.h", "e4m3.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_199_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
