@@ -1,0 +1,60 @@
+"""The benchmark's own arithmetic, on the CPU: the byte and flop counts behind `value` and `roofline`
+against brute-force counts on small workloads, and the single-GPU contract of the command line."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from paged_kv_cache_199_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _brute_kv_bytes(w):
+    """K+V bytes with every (physical block, slot) that some sequence attends counted once."""
+    e = 1 if w.kv_fp8 else (4 if w.spec.dtype == "f32" else 2)
+    seen = set()
+    for s in range(w.num_seqs):
+        for t in range(int(w.context_lens[s])):
+            seen.add((int(w.block_tables[s, t // 16]), t % 16))
+    return len(seen) * w.spec.num_kv_heads * w.spec.head_dim * 2 * e
+
+
+def test_algorithmic_bytes_count_shared_pages_once():
+    spec = W.custom("acct", [5, 40, 33, 64], q_len=[1, 2, 1, 3], num_heads=8, num_kv_heads=2, head_dim=64,
+                    shared_prefix_blocks=2)
+    w = W.build(spec, "cpu")
+    B, H, D = 16, 8, 64
+    kv = _brute_kv_bytes(w)
+    qo = w.total_q * H * D * 2 * 2 + w.total_q * H * 4
+    meta = sum((int(c) + B - 1) // B for c in w.context_lens) * 4 + w.num_seqs * 8
+    assert bench.algorithmic_bytes(w) == kv + qo + meta
+    assert bench.logical_kv_bytes(w) == int(w.context_lens.sum()) * 2 * D * 2 * 2 > kv
+
+
+def test_write_bytes_and_fp8_element_size():
+    w = W.build(W.custom("acct8", [17, 3], num_heads=4, num_kv_heads=2, head_dim=64, kv_fp8=True,
+                         write_new_token=True), "cpu")
+    # the new rows are read as bf16 (2 bytes) and written as codes (1 byte), plus their slots
+    assert bench.write_bytes(w) == 2 * 2 * 64 * (2 + 1) * 2 + 2 * 8
+    assert bench.algorithmic_bytes(w) - bench.algorithmic_bytes(W.build(W.custom(
+        "acct16", [17, 3], num_heads=4, num_kv_heads=2, head_dim=64), "cpu")) == -_brute_kv_bytes(w)
+
+
+def test_prefill_flops_is_the_sum_over_visible_pairs():
+    spec = W.custom("pf", [7, 40, 300], q_len=[7, 16, 100], num_heads=4, num_kv_heads=2, head_dim=32)
+    w = W.build(spec, "cpu")
+    pairs = 0
+    for s in range(w.num_seqs):
+        n, q = int(w.context_lens[s]), int(w.q_lens[s])
+        for i in range(q):
+            pairs += n - q + i + 1             # keys 0 .. n - q + i
+    assert bench.prefill_flops(w) == pairs * 4 * 4 * 32
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
