@@ -66,7 +66,7 @@ struct PrefixArgs {
   int32_t *sfx_table;            // [num_seqs, sfx_stride]
   int sfx_stride;                // ceil(max_context_len / 16)
   const int32_t *q_start;        // NULL: s * max_q_len
-  float *sfx_lse;                // [total_q, H], natural log, written by the suffix pass
+  float *sfx_lse;                // [total_q, H]: the suffix pass's natural-log LSE when the caller wants none
   float *pre_o;                  // [items * 32, D]
   float *pre_lse;                // [items * 32], log2
 };
@@ -90,6 +90,34 @@ __device__ __forceinline__ SeqInfo load_seq(const DecodeArgs &a, int s) {
   si.qbase = a.q_start ? a.q_start[s] : s * a.max_q_len;
   si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
   return si;
+}
+
+// Group g's prefix in whole pages, within max_prefix_len.
+__device__ __forceinline__ int prefix_tokens(const PrefixArgs &p, int g) {
+  return min(max(p.prefix_lens[g], 0), p.max_prefix_len) / 16 * 16;
+}
+
+// Group holding sequence s (the last g with starts[g] <= s, if s < starts[num_groups]) and its
+// clamped bounds; -1 when s is in no group or past the group's first max_group_size members.
+__device__ __forceinline__ int group_of(const DecodeArgs &a, const PrefixArgs &p, int s, int &gs, int &pg) {
+  const int S = a.num_seqs;
+  auto start = [&](int g) { return min(max(p.group_starts[g], 0), S); };
+  if (p.num_groups <= 0 || s < start(0) || s >= start(p.num_groups)) return -1;
+  int g0 = 0, g1 = p.num_groups;
+  while (g1 - g0 > 1) {
+    const int mid = (g0 + g1) >> 1;
+    if (start(mid) <= s) g0 = mid;
+    else g1 = mid;
+  }
+  gs = start(g0);
+  if (s - gs >= p.max_group_size) return -1;
+  pg = prefix_tokens(p, g0);
+  return g0;
+}
+
+// Shared length of sequence s: the group's prefix, cut to the whole pages before its new tokens.
+__device__ __forceinline__ int shared_len(const SeqInfo &si, int pg) {
+  return min(pg, (si.ctx - si.qs) / 16 * 16);
 }
 
 // The balanced schedule's page stream: for each kv head, for each sequence, for each row tile, the

@@ -16,8 +16,49 @@ namespace pkv {
 // weight sum are wave reductions, and the weights and row offsets are broadcast from the lane that
 // holds them, so the partial outputs stream with several loads in flight instead of one dependent
 // load per source.
-template <bool BF16, int D>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+//
+// PRE (read-once shared-prefix decode): this pass attended each sequence's keys past its shared
+// prefix; a row whose sequence shares a prefix is then merged, by the same rule, with the prefix
+// pass's chunk partials (p.pre_o / p.pre_lse), whether its own result came out of this merge or was
+// already final in out / lse.
+template <int D>
+__device__ __forceinline__ void merge_prefix_chunks(const DecodeArgs &a, const PrefixArgs &p, int64_t base, int lane,
+                                                    const float *o_s, float l2s, int nc, int64_t crow0,
+                                                    int64_t cstride) {
+  constexpr int DPL = D / 64;
+  const float l = lane < nc ? p.pre_lse[crow0 + lane * cstride] : -INFINITY;
+  const float mx = fmaxf(wave_max(l), l2s);
+  const float wl = exp2_hw(l - mx);                         // 0 on lanes past nc
+  const float ws = exp2_hw(l2s - mx);
+  const float wsum = wave_sum(wl) + ws;
+  float acc[DPL];
+  #pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = ws * o_s[k];
+  const float *po = p.pre_o + crow0 * D + lane;
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    float v[8][DPL];
+    #pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = min(c0 + u, nc - 1);
+      #pragma unroll
+      for (int k = 0; k < DPL; ++k) v[u][k] = po[c * cstride * D + 64 * k];
+    }
+    #pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wc = c0 + u < nc ? __shfl(wl, c0 + u) : 0.f;
+      #pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wc, v[u][k], acc[k]);
+    }
+  }
+  const float inv = 1.f / wsum;
+  uint16_t *out = static_cast<uint16_t *>(a.out) + base * D + lane;
+  #pragma unroll
+  for (int k = 0; k < DPL; ++k) out[64 * k] = f32_to_bf16(acc[k] * inv);
+  if (lane == 0 && a.lse) a.lse[base] = (mx + log2_hw(wsum)) * kLn2;
+}
+
+template <bool BF16, int D, bool PRE>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, PrefixArgs p) {
   constexpr int DPL = D / 64;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -38,6 +79,24 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (row >= a.total_q) return;
   const int64_t stride = (int64_t)a.total_q * H;          // between partitions
   const int64_t base = (int64_t)row * H + h;
+  // read-once decode: the prefix chunks this row merges (none when its sequence shares nothing)
+  int nc = 0;
+  int64_t crow0 = 0, cstride = 0;
+  if constexpr (PRE) {
+    int gs = 0, pg = 0;
+    const int g = group_of(a, p, s, gs, pg);
+    const int ps = g >= 0 ? p.skip[s] : 0;
+    const int G = a.group;
+    const int kvh = h / G;
+    const int gr = ((s - gs) * a.max_q_len + i) * G + (h - kvh * G);
+    if (ps > 0 && gr < p.rows_max && p.chunk_pages > 0) {
+      nc = min((ps / kBlock + p.chunk_pages - 1) / p.chunk_pages, p.chunks);
+      const int rt = gr / kPrefixRows;
+      crow0 = ((((int64_t)g * a.num_kv_heads + kvh) * p.chunks) * p.row_tiles + rt) * kPrefixRows +
+              (gr - rt * kPrefixRows);
+      cstride = (int64_t)p.row_tiles * kPrefixRows;
+    }
+  }
 
   // shares that start inside this row's work item [pos0, pos1) of the balanced stream
   int ncand = 0, ord0 = 0, srow = 0;
@@ -90,7 +149,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     any_cut = __builtin_amdgcn_ballot_w64(cut) != 0;
   }
   // a row whose item one wave covered in one piece already holds its final output
-  if (si.nparts <= 1 && !any_cut) return;
+  if (si.nparts <= 1 && !any_cut) {
+    if constexpr (PRE) {
+      if (nc > 0) {
+        float o_s[DPL];
+        const uint16_t *os = static_cast<const uint16_t *>(a.out) + base * D + lane;
+        #pragma unroll
+        for (int k = 0; k < DPL; ++k) o_s[k] = __uint_as_float((uint32_t)os[64 * k] << 16);
+        merge_prefix_chunks<D>(a, p, base, lane, o_s, a.lse[base] * kLog2e, nc, crow0, cstride);
+      }
+    }
+    return;
+  }
 
   float acc[DPL];
   #pragma unroll
@@ -177,6 +247,15 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   L2 = wave_sum(L2);
   const bool seen = L2 > 0.f;
   const float inv = seen ? 1.f / L2 : 0.f;
+  if constexpr (PRE) {
+    if (nc > 0) {
+      float o_s[DPL];
+      #pragma unroll
+      for (int k = 0; k < DPL; ++k) o_s[k] = acc[k] * inv;
+      merge_prefix_chunks<D>(a, p, base, lane, o_s, seen ? Ms + log2_hw(L2) : -INFINITY, nc, crow0, cstride);
+      return;
+    }
+  }
   #pragma unroll
   for (int k = 0; k < DPL; ++k) {
     const float o = acc[k] * inv;
@@ -214,15 +293,20 @@ __global__ __launch_bounds__(1024) void q_start_kernel(const int32_t *q_lens, in
   if (tid == 1023) q_start[n] = part[1023];
 }
 
-hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st) {
+// pre: the read-once decode's prefix pass to merge (bf16 only), or nullptr.
+hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, const PrefixArgs *pre, hipStream_t st) {
   const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * a.num_heads;
   const int grid = (int)((waves + 3) / 4);
-  if (bf16) {
-    if (head_dim == 64) combine_kernel<true, 64><<<grid, 256, 0, st>>>(a);
-    else combine_kernel<true, 128><<<grid, 256, 0, st>>>(a);
+  const PrefixArgs none{};
+  if (pre) {
+    if (head_dim == 64) combine_kernel<true, 64, true><<<grid, 256, 0, st>>>(a, *pre);
+    else combine_kernel<true, 128, true><<<grid, 256, 0, st>>>(a, *pre);
+  } else if (bf16) {
+    if (head_dim == 64) combine_kernel<true, 64, false><<<grid, 256, 0, st>>>(a, none);
+    else combine_kernel<true, 128, false><<<grid, 256, 0, st>>>(a, none);
   } else {
-    if (head_dim == 64) combine_kernel<false, 64><<<grid, 256, 0, st>>>(a);
-    else combine_kernel<false, 128><<<grid, 256, 0, st>>>(a);
+    if (head_dim == 64) combine_kernel<false, 64, false><<<grid, 256, 0, st>>>(a, none);
+    else combine_kernel<false, 128, false><<<grid, 256, 0, st>>>(a, none);
   }
   return hipGetLastError();
 }

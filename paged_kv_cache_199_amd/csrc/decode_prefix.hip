@@ -18,41 +18,13 @@
 //           workgroup are four row tiles of one chunk and read its pages from LDS, staged once
 //           (lds_pages.h); over E4M3 pools each wave streams and widens its pages itself.  Each wave
 //           leaves an fp32 partial row and its log2 LSE.
-//   merge:  per (sequence, new token, head): the suffix result (already in out, with a natural-log
-//           LSE) merged with the row's prefix chunks.
+//   merge:  in the suffix pass's split-K combine (decode_combine.hip): each row's suffix result
+//           merged with its prefix chunks by the same log-sum-exp rule.
 #include "decode_args.h"
 #include "device_common.h"
 #include "lds_pages.h"
 
 namespace pkv {
-
-// Group g's prefix in whole pages, within max_prefix_len.
-__device__ __forceinline__ int prefix_tokens(const PrefixArgs &p, int g) {
-  return min(max(p.prefix_lens[g], 0), p.max_prefix_len) / kBlock * kBlock;
-}
-
-// Group holding sequence s (the last g with starts[g] <= s, if s < starts[num_groups]) and its
-// clamped bounds; -1 when s is in no group or past the group's first max_group_size members.
-__device__ __forceinline__ int group_of(const DecodeArgs &a, const PrefixArgs &p, int s, int &gs, int &pg) {
-  const int S = a.num_seqs;
-  auto start = [&](int g) { return min(max(p.group_starts[g], 0), S); };
-  if (p.num_groups <= 0 || s < start(0) || s >= start(p.num_groups)) return -1;
-  int g0 = 0, g1 = p.num_groups;
-  while (g1 - g0 > 1) {
-    const int mid = (g0 + g1) >> 1;
-    if (start(mid) <= s) g0 = mid;
-    else g1 = mid;
-  }
-  gs = start(g0);
-  if (s - gs >= p.max_group_size) return -1;
-  pg = prefix_tokens(p, g0);
-  return g0;
-}
-
-// Shared length of sequence s: the group's prefix, cut to the whole pages before its new tokens.
-__device__ __forceinline__ int shared_len(const SeqInfo &si, int pg) {
-  return min(pg, (si.ctx - si.qs) / kBlock * kBlock);
-}
 
 // One wave per sequence: P_s, the suffix row of the block table and the suffix length.
 __device__ __forceinline__ void prefix_prep(const DecodeArgs &a, const PrefixArgs &p, int s, int lane) {
@@ -223,74 +195,6 @@ __global__ __launch_bounds__(256) void prefix_attend_f8_kernel(DecodeArgs a, Pre
       [&](int, uint4 *, uint2 *) {});
 }
 
-// One wave per (sequence, new token, head).  The row's chunk LSEs are read at once (lane c holds chunk
-// c; the plan keeps chunks <= 64), their max and weight sum are wave reductions, and the partial rows
-// stream with the weights broadcast from the lanes that hold them, eight loads in flight.
-template <int D>
-__global__ __launch_bounds__(256) void prefix_merge_kernel(DecodeArgs a, PrefixArgs p) {
-  constexpr int DPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int H = a.num_heads;
-  if (wid >= (int64_t)a.num_seqs * a.max_q_len * H) return;
-  const int h = (int)(wid % H);
-  const int i = (int)((wid / H) % a.max_q_len);
-  const int s = (int)(wid / ((int64_t)H * a.max_q_len));
-  const SeqInfo si = load_seq(a, s);
-  if (i >= si.qs) return;
-  const int qrow = (p.q_start ? p.q_start[s] : s * a.max_q_len) + i;
-  if (qrow >= a.total_q) return;
-  const int64_t orow = (int64_t)qrow * H + h;
-  const int G = a.group;
-  const int kvh = h / G;
-  const int hg = h - kvh * G;
-  int gs = 0, pg = 0;
-  const int g = group_of(a, p, s, gs, pg);
-  const int ps = g >= 0 ? shared_len(si, pg) : 0;
-  const int nc = min((ps / kBlock + p.chunk_pages - 1) / p.chunk_pages, p.chunks);   // chunks with keys < P_s
-  const int gr = ((s - gs) * a.max_q_len + i) * G + hg;
-  const float lse_s = p.sfx_lse[orow];
-  if (nc <= 0 || gr >= p.rows_max) {
-    // no shared keys: the suffix pass's result is the answer
-    if (lane == 0 && a.lse) a.lse[orow] = lse_s;
-    return;
-  }
-  const int rt = gr / kPrefixRows;
-  const int64_t prow0 = ((((int64_t)g * a.num_kv_heads + kvh) * p.chunks) * p.row_tiles + rt) * kPrefixRows +
-                        (gr - rt * kPrefixRows);
-  const int64_t cstride = (int64_t)p.row_tiles * kPrefixRows;    // between chunks of one row
-  const float l2s = lse_s * kLog2e;
-  const float l = lane < nc ? p.pre_lse[prow0 + lane * cstride] : -INFINITY;
-  const float mx = fmaxf(wave_max(l), l2s);
-  const float wl = exp2_hw(l - mx);                               // 0 on lanes past nc
-  const float ws = exp2_hw(l2s - mx);
-  const float wsum = wave_sum(wl) + ws;
-  uint16_t *out = static_cast<uint16_t *>(a.out) + orow * D + lane * DPL;
-  float acc[DPL];
-  #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = ws * __uint_as_float((uint32_t)out[e] << 16);
-  const float *po = p.pre_o + prow0 * D + lane * DPL;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
-    float v[8][DPL];
-    #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = min(c0 + u, nc - 1);
-      #pragma unroll
-      for (int e = 0; e < DPL; ++e) v[u][e] = po[c * cstride * D + e];
-    }
-    #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wc = c0 + u < nc ? __shfl(wl, c0 + u) : 0.f;
-      #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += wc * v[u][e];
-    }
-  }
-  const float inv = 1.f / wsum;
-  #pragma unroll
-  for (int e = 0; e < DPL; ++e) out[e] = f32_to_bf16(acc[e] * inv);
-  if (lane == 0 && a.lse) a.lse[orow] = (mx + log2_hw(wsum)) * kLn2;
-}
-
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st) {
   const int64_t tiles = p.chunks > 0 ? (int64_t)p.num_groups * a.num_kv_heads * p.chunks : 0;
   // bf16: a workgroup per four row tiles; E4M3: a wave per row tile
@@ -303,14 +207,6 @@ hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int he
     if (f8) prefix_attend_f8_kernel<128, 2><<<grid, 256, 0, st>>>(a, p, item_wgs);
     else prefix_attend_lds_kernel<128><<<grid, 256, 0, st>>>(a, p, item_wgs);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_prefix_merge(const DecodeArgs &a, const PrefixArgs &p, int head_dim, hipStream_t st) {
-  const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * a.num_heads;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (head_dim == 64) prefix_merge_kernel<64><<<grid, 256, 0, st>>>(a, p);
-  else prefix_merge_kernel<128><<<grid, 256, 0, st>>>(a, p);
   return hipGetLastError();
 }
 

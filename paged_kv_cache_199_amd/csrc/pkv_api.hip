@@ -25,11 +25,10 @@ int mfma_rows_per_tile(int rows);
 int mfma_default_depth(int head_dim, int rows_per_tile, bool persistent);
 int persistent_max_seqs();
 int mfma_persistent_wgs_per_cu(int head_dim, int rows_per_tile, int depth, int num_seqs);
-hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
+hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, const PrefixArgs *pre, hipStream_t st);
 hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st);
-hipError_t launch_prefix_merge(const DecodeArgs &a, const PrefixArgs &p, int head_dim, hipStream_t st);
 hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, hipStream_t st);
 }  // namespace pkv
 
@@ -277,13 +276,14 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
 
 namespace {
 
-// Shared body of pkv_paged_attn_decode and pkv_paged_attn_decode_append (new_k / new_v NULL: no append).
+// Shared body of pkv_paged_attn_decode and pkv_paged_attn_decode_append (new_k / new_v NULL: no append),
+// and the per-sequence pass of the read-once decode (pre: its prefix pass, merged in the combine).
 int decode_impl(const void *q, const void *new_k, const void *new_v, const void *k_cache, const void *v_cache,
                 const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_lens, void *out,
                 float *lse, int num_seqs, int max_blocks_per_seq, int total_q, int max_q_len,
                 int max_context_len, int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
                 int block_size, float scale, int dtype, const pkv_decode_options *opts, void *workspace,
-                size_t workspace_bytes, void *stream) {
+                size_t workspace_bytes, void *stream, const pkv::PrefixArgs *pre = nullptr) {
   if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
                               head_dim, dtype, opts);
@@ -381,8 +381,8 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   if (opts && opts->event_main_end &&
       hipEventRecord(static_cast<hipEvent_t>(opts->event_main_end), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
-  if (pl.num_parts > 1 || persist) {
-    if (pkv::launch_combine(a, bf16, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  if (pl.num_parts > 1 || persist || pre) {
+    if (pkv::launch_combine(a, bf16, head_dim, pre, s) != hipSuccess) return PKV_ERR_LAUNCH;
   }
   return PKV_OK;
 }
@@ -613,14 +613,12 @@ int pkv_paged_attn_decode_shared_prefix(const void *q, const void *k_cache, cons
     return PKV_ERR_LAUNCH;
   // the shared pass, with the suffix tables built by extra workgroups of the same launch
   if (pkv::launch_prefix_attend(a, p, head_dim, dtype == PKV_BF16_FP8KV, s) != hipSuccess) return PKV_ERR_LAUNCH;
-  // every sequence's own keys: the ordinary decode over the suffix tables, its LSE kept for the merge
-  const int rc = decode_impl(q, nullptr, nullptr, k_cache, v_cache, p.sfx_table, p.sfx_ctx, q_lens, out, p.sfx_lse,
-                             num_seqs, pp.sfx_stride, total_q, max_q_len, max_context_len, num_blocks, num_heads,
-                             num_kv_heads, head_dim, block_size, scale, dtype, opts, ws + pp.off_decode,
-                             pp.decode_bytes, stream);
-  if (rc != PKV_OK) return rc;
-  if (pkv::launch_prefix_merge(a, p, head_dim, s) != hipSuccess) return PKV_ERR_LAUNCH;
-  return PKV_OK;
+  // every sequence's own keys: the ordinary decode over the suffix tables; its combine merges the
+  // prefix chunks in (the merge reads the suffix LSE, so one is kept when the caller wants none)
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, p.sfx_table, p.sfx_ctx, q_lens, out,
+                     lse ? lse : p.sfx_lse, num_seqs, pp.sfx_stride, total_q, max_q_len, max_context_len, num_blocks,
+                     num_heads, num_kv_heads, head_dim, block_size, scale, dtype, opts, ws + pp.off_decode,
+                     pp.decode_bytes, stream, &p);
 }
 
 }  // extern "C"
