@@ -319,9 +319,11 @@ def bench_prefill(args, dev, spec):
     lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
     q_lens = None if w.uniform_q else meta["q_lens"]
 
+    scales = dict(k_scale=spec.k_scale, v_scale=spec.v_scale) if spec.kv_fp8 else {}
+
     def step():
         _lib.paged_attn_prefill(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"], q_lens, out,
-                                lse, H, KVH, D, spec.block_size, w.scale, w.max_context_len, w.max_q_len)
+                                lse, H, KVH, D, spec.block_size, w.scale, w.max_context_len, w.max_q_len, **scales)
 
     for _ in range(args.warmup):
         step()
@@ -362,7 +364,8 @@ def bench_prefill(args, dev, spec):
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V, shuffled 16-token pages)",
         "config": {"workload": spec.name, "num_seqs": w.num_seqs, "num_heads": H, "num_kv_heads": KVH,
-                   "head_dim": D, "block_size": spec.block_size, "new_tokens": int(w.q_lens.sum()),
+                   "head_dim": D, "block_size": spec.block_size, "kv_cache": "e4m3" if spec.kv_fp8 else "bf16",
+                   "new_tokens": int(w.q_lens.sum()),
                    "context_tokens": int(w.context_lens.astype(np.int64).sum()),
                    "max_context_len": w.max_context_len},
         "new_tokens_per_s": round(int(w.q_lens.sum()) / (ms * 1e-3), 1),
@@ -382,7 +385,14 @@ def bench_prefill(args, dev, spec):
             t = t.detach().cpu().contiguous()
             return t.view(torch.int16).numpy().view(np.uint16)
 
-        qh, kc, vc = bits(w.q), bits(w.k_cache), bits(w.v_cache)
+        qh = bits(w.q)
+        if spec.kv_fp8:
+            from oracle import fp8 as F8
+
+            kc = F8.dequantize(w.k_cache.cpu().numpy(), spec.k_scale)
+            vc = F8.dequantize(w.v_cache.cpu().numpy(), spec.v_scale)
+        else:
+            kc, vc = bits(w.k_cache), bits(w.v_cache)
         done, t_used, n = 0, 0.0, 0
         with threadpool_limits(limits=1):
             while t_used < min(args.cpu_budget, 20.0):

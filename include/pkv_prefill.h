@@ -24,17 +24,19 @@ extern "C" {
 
 /*
  * Arguments, layouts and preconditions as pkv_paged_attn_decode (q_lens NULL: every sequence has
- * max_q_len new tokens); no workspace.  dtype: PKV_BF16 only.  Writes out [total_q, H, D] and, when
- * lse is not NULL, lse [total_q, H] (natural log).  Errors: PKV_ERR_UNSUPPORTED for another dtype,
- * head_dim or block_size; PKV_ERR_SHAPE / PKV_ERR_NULL as pkv_paged_attn_decode; PKV_ERR_LAUNCH.
- * Enqueued on `stream`; nothing is allocated or synchronized.
+ * max_q_len new tokens); no workspace.  dtype: PKV_BF16, or PKV_BF16_FP8KV (E4M3 pools, their scales
+ * in opts->k_scale / v_scale; opts may be NULL, and its other fields are ignored here).  Writes out
+ * [total_q, H, D] and, when lse is not NULL, lse [total_q, H] (natural log).  Errors:
+ * PKV_ERR_UNSUPPORTED for another dtype, head_dim or block_size or a bad scale; PKV_ERR_SHAPE /
+ * PKV_ERR_NULL as pkv_paged_attn_decode; PKV_ERR_LAUNCH.  Enqueued on `stream`; nothing is allocated
+ * or synchronized.
  */
 int pkv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
                            const int32_t *block_tables, const int32_t *context_lens, const int32_t *q_lens,
                            void *out, float *lse, int num_seqs, int max_blocks_per_seq, int total_q,
                            int max_q_len, int max_context_len, int64_t num_blocks, int num_heads,
                            int num_kv_heads, int head_dim, int block_size, float scale, int dtype,
-                           void *stream);
+                           const pkv_decode_options *opts, void *stream);
 
 #ifdef __cplusplus
 }

@@ -61,7 +61,8 @@ EXPORTS = {
                                                      _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                                      ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
     "pkv_paged_attn_prefill": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
-                                        _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
+                                        _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
+                                        ctypes.POINTER(DecodeOptions), _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, _c_i64, _c_int, _c_int, _c_int, _vp]),
     # host-side block management (include/pkv_blocks.h); handles are opaque pointers
     "pkv_block_pool_create": (_vp, [ctypes.c_int32]),
@@ -345,9 +346,11 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_l
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
-                       num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len, stream=None) -> None:
+                       num_kv_heads, head_dim, block_size, scale, max_context_len, max_q_len, stream=None,
+                       k_scale: float = 0.0, v_scale: float = 0.0) -> None:
     """Prefill / chunked-prefill attention through the C ABI (include/pkv_prefill.h): bf16 q/out
-    [total_q, H, D] over bf16 pools; the new tokens' K/V already written to the cache."""
+    [total_q, H, D] over bf16 pools or uint8 E4M3 pools (with their scales); the new tokens' K/V
+    already written to the cache."""
     lib = load()
     _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
     total_q = q.shape[0]
@@ -365,10 +368,11 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, q_lens, 
     if lse is not None:
         _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
               "lse: fp32 [total_q, H]")
+    o = _opts(0, PATH_AUTO, None, k_scale=k_scale, v_scale=v_scale)
     rc = lib.pkv_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                                     _ptr(q_lens), _ptr(out), _ptr(lse), S, block_tables.shape[1], total_q, max_q_len,
                                     max_context_len, NB, num_heads, num_kv_heads, head_dim, block_size,
-                                    float(scale), code, _stream(stream))
+                                    float(scale), code, ctypes.byref(o), _stream(stream))
     _check(rc, "pkv_paged_attn_prefill")
 
 

@@ -9,6 +9,8 @@
 // one read instruction pairs up (d and d + 8) sit in different banks.
 #pragma once
 
+#include <type_traits>
+
 #include "mfma_wave.h"
 
 #ifndef PKV_LDS_KPAD
@@ -34,13 +36,17 @@ struct LdsPages {
 // Logical pages [jb, je) of block-table row bt (kv head kvh) through LDS buffer `lds`
 // (LdsPages<D, SP>::BYTES).  Every thread of the workgroup must call it (it holds barriers); this
 // wave computes the pages j < jw with its rows (jw <= je; a wave with no rows passes jw = jb).
-template <int D, int NT, int SP>
+// F8: the pools hold E4M3 codes; each 16-code chunk is widened exactly to bf16 as it is staged, so
+// LDS and everything after it are as for bf16 pools (the pools' scales sit in the score scale and
+// the epilogue).
+template <int D, int NT, int SP, bool F8 = false>
 __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
                                                  const int32_t *bt, int jb, int je, int jw, char *lds,
                                                  const WaveRows<D, NT> &w, WaveAcc<D, NT> &st) {
   typedef LdsPages<D, SP> L;
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
+  constexpr int EB = F8 ? 1 : 2;               // bytes per cache element
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int col = lane & 15;
@@ -50,10 +56,12 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
   const int nstages = (n + SP - 1) / SP;
   const char *kbase = static_cast<const char *>(a.k_cache);
   const char *vbase = static_cast<const char *>(a.v_cache);
-  const int64_t page_bytes = (int64_t)kBlock * L::ROWB;
-  // each thread moves one 16-byte chunk of every K page and one of every V page (D = 64: threads < 128)
-  const bool mover = tid < kBlock * L::CH;
-  uint4 kn[SP], vn[SP];
+  const int64_t page_bytes = (int64_t)kBlock * D * EB;
+  // each thread moves 8 elements of every K page and 8 of every V page (a 16-byte chunk of bf16, or
+  // 8 bytes of codes); D = 64: threads < 128
+  typedef typename std::conditional<F8, uint2, uint4>::type Chunk;
+  const bool mover = tid < kBlock * D / 8;
+  Chunk kn[SP], vn[SP];
   int okn = 0;                               // bit p: page p of the stage has a valid id
   auto fetch = [&](int stage) {
     okn = 0;
@@ -63,10 +71,10 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
       const int bid = bt[j];
       const bool ok = bid >= 0 && bid < a.num_blocks;
       okn |= ok ? 1 << p : 0;
-      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * 16;
+      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * (int)sizeof(Chunk);
       if (mover) {
-        kn[p] = ld16(kbase + off);
-        vn[p] = ld16(vbase + off);
+        kn[p] = *reinterpret_cast<const Chunk *>(kbase + off);
+        vn[p] = *reinterpret_cast<const Chunk *>(vbase + off);
       }
     }
   };
@@ -75,12 +83,26 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
       #pragma unroll
       for (int p = 0; p < SP; ++p) {
         char *pg = lds + (b * SP + p) * L::PBYTES;
-        *reinterpret_cast<uint4 *>(pg + (tid / L::CH) * L::KPAD + (tid % L::CH) * 16) = kn[p];
+        // widened to 8 bf16 (F8: exact), the thread's elements are in the bf16 page's order
+        uint4 k8, v8;
+        if constexpr (F8) {
+          k8 = make_uint4(fp8x2_to_bf16x2<false>(kn[p].x), fp8x2_to_bf16x2<true>(kn[p].x),
+                          fp8x2_to_bf16x2<false>(kn[p].y), fp8x2_to_bf16x2<true>(kn[p].y));
+          v8 = make_uint4(fp8x2_to_bf16x2<false>(vn[p].x), fp8x2_to_bf16x2<true>(vn[p].x),
+                          fp8x2_to_bf16x2<false>(vn[p].y), fp8x2_to_bf16x2<true>(vn[p].y));
+        } else {
+          k8 = kn[p];
+          v8 = vn[p];
+        }
+        // K: elements 8 tid .. +7 are dims (8 tid) % D .. +7 of token 8 tid / D
+        *reinterpret_cast<uint4 *>(pg + (tid / L::CH) * L::KPAD + (tid % L::CH) * 16) = k8;
+        // V: elements 8 tid .. +7 are tokens 8 (tid & 1) .. +7 of dim tid / 2, i.e. its 4-token groups
+        // 2 (tid & 1) and 2 (tid & 1) + 1, stored in slots group ^ vswz(dim)
         const int d = tid >> 1;
         const int g0 = ((tid & 1) * 2) ^ vswz(d);
         char *vrow = pg + L::KBYTES + d * L::VROW;
-        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(vn[p].x, vn[p].y);
-        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(vn[p].z, vn[p].w);
+        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(v8.x, v8.y);
+        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(v8.z, v8.w);
       }
     }
   };

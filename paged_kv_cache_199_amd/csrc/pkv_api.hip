@@ -29,7 +29,7 @@ hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, const Pr
 hipError_t launch_kv_append(const DecodeArgs &a, bool bf16, int head_dim, hipStream_t st);
 hipError_t launch_q_start(const int32_t *q_lens, int32_t *q_start, int n, hipStream_t st);
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st);
-hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, hipStream_t st);
+hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, bool f8, hipStream_t st);
 }  // namespace pkv
 
 namespace {
@@ -629,8 +629,9 @@ int pkv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cac
                            const int32_t *context_lens, const int32_t *q_lens, void *out, float *lse, int num_seqs,
                            int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
                            int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                           float scale, int dtype, void *stream) {
-  if (block_size != kBlockSize || dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+                           float scale, int dtype, const pkv_decode_options *opts, void *stream) {
+  if (block_size != kBlockSize || (dtype != PKV_BF16 && dtype != PKV_BF16_FP8KV)) return PKV_ERR_UNSUPPORTED;
+  if (opts && (!valid_scale(opts->k_scale) || !valid_scale(opts->v_scale))) return PKV_ERR_UNSUPPORTED;
   const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
                               dtype, nullptr);
   if (st != PKV_OK) return st;
@@ -664,13 +665,21 @@ int pkv_paged_attn_prefill(const void *q, const void *k_cache, const void *v_cac
   a.group = G;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.v_scale = 1.f;
+  a.k_scale = 1.f;
+  const bool f8 = dtype == PKV_BF16_FP8KV;
+  if (f8) {
+    // the pools' scales factor out of the products: K's into the scores, V's into the epilogue
+    a.k_scale = opts && opts->k_scale > 0.f ? opts->k_scale : 1.f;
+    a.scale_log2 *= a.k_scale;
+    a.v_scale = opts && opts->v_scale > 0.f ? opts->v_scale : 1.f;
+  }
   a.part_size = max_context_len;
   a.num_parts = 1;
   a.row_tiles = (int)row_blocks;
   a.units = (int)units;
   a.per_xcd = ceil_div(units, 8);
-  return pkv::launch_prefill_mfma(a, head_dim, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
-                                                                                                : PKV_ERR_LAUNCH;
+  return pkv::launch_prefill_mfma(a, head_dim, f8, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK
+                                                                                                    : PKV_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// Paged prefill / chunked prefill attention on the matrix cores (bf16).
+// Paged prefill / chunked prefill attention on the matrix cores (bf16, over bf16 or E4M3 pools).
 //
 // The same operation as decode (every new token of a sequence attends the cached tokens and the new
 // tokens up to itself, through the block table), with many new tokens per sequence: a prompt, or a
@@ -26,7 +26,7 @@ namespace pkv {
 constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
-template <int D, int SP>
+template <int D, int SP, bool F8>
 __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   constexpr int NT = kPrefillNT;
   constexpr int WROWS = 16 * NT;             // rows per wave
@@ -72,14 +72,20 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
   init_acc<D, NT>(st);
 
   const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  lds_stream_pages<D, NT, SP>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
+  lds_stream_pages<D, NT, SP, F8>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
   if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
 }
 
-hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, hipStream_t st) {
+// f8: E4M3 pools (pages widened to bf16 as they are staged).
+hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, bool f8, hipStream_t st) {
   const dim3 grid((unsigned)(a.per_xcd * 8));
-  if (head_dim == 64) prefill_mfma_kernel<64, 4><<<grid, 256, 0, st>>>(a);
-  else prefill_mfma_kernel<128, 4><<<grid, 256, 0, st>>>(a);
+  if (head_dim == 64) {
+    if (f8) prefill_mfma_kernel<64, 4, true><<<grid, 256, 0, st>>>(a);
+    else prefill_mfma_kernel<64, 4, false><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (f8) prefill_mfma_kernel<128, 4, true><<<grid, 256, 0, st>>>(a);
+    else prefill_mfma_kernel<128, 4, false><<<grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

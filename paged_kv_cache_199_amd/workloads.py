@@ -91,6 +91,8 @@ NAMED: List[Spec] = [
          kv_fp8=True),
     Spec("long_ctx_fp8kv", 256, 64, 8, 128, "bf16", ctx=("lognormal", 4096, 0.8, 64, 32768), seed=1004,
          kv_fp8=True),
+    Spec("prefill_chunk_fp8kv", 16, 32, 8, 128, "bf16", ctx=("uniform", 512, 4096), q_len=512, seed=1006,
+         prefill=True, kv_fp8=True),
 ]
 
 

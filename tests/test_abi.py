@@ -175,8 +175,8 @@ def test_prefill_argument_validation(lib):
 
     def call(dt=1, D=128, B=16, S=4, q=f, mq=256, tq=1024):
         return lib.pkv_paged_attn_prefill(q, f, f, f, f, None, f, None, S, 64, tq, mq, 1024, 64, 32, 8, D, B, 0.1, dt,
-                                          None)
-    assert call(dt=0) == -3 and call(dt=2) == -3      # bf16 pools only
+                                          None, None)
+    assert call(dt=0) == -3                           # bf16 q/out (over bf16 or E4M3 pools)
     assert call(D=96) == -3 and call(B=8) == -3
     assert call(q=None) == -1
     assert call(tq=1000) == -2                        # q_lens NULL: total_q = num_seqs * max_q_len

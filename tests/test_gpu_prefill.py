@@ -1,7 +1,8 @@
 """Paged prefill / chunked prefill (pkv_paged_attn_prefill) against the float64 oracle: the same
 definition as decode (oracle.paged_attention.paged_decode_attention) with many new tokens per
-sequence.  Bars: max |delta| <= 1.5e-2 on bf16 outputs, LSE within 2e-3.  Pools are poisoned (NaN in
-every slot no sequence may read), so a read past a sequence's context or its causal limit shows."""
+sequence, over bf16 pools and over E4M3 pools (the oracle reads the values the codes stand for).
+Bars: max |delta| <= 1.5e-2 on bf16 outputs, LSE within 2e-3.  Pools are poisoned (NaN in every slot
+no sequence may read), so a read past a sequence's context or its causal limit shows."""
 import numpy as np
 import pytest
 import torch
@@ -23,9 +24,10 @@ def _prefill(w, ragged=None):
     out = torch.empty_like(w.q)
     lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=DEV)
     use_qlens = (not w.uniform_q) if ragged is None else ragged
+    scales = dict(k_scale=w.spec.k_scale, v_scale=w.spec.v_scale) if w.kv_fp8 else {}
     _lib.paged_attn_prefill(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"],
                             meta["q_lens"] if use_qlens else None, out, lse, w.spec.num_heads, w.spec.num_kv_heads,
-                            w.spec.head_dim, 16, w.scale, w.max_context_len, w.max_q_len)
+                            w.spec.head_dim, 16, w.scale, w.max_context_len, w.max_q_len, **scales)
     torch.cuda.synchronize()
     return out, lse
 
@@ -63,6 +65,28 @@ def test_chunked_prefill_workload_sampled(gpu_lib):
     w = W.build("prefill_chunk_bf16", DEV)
     seqs = [0, 5, 11, 15]
     _say(f"[case] prefill_chunk_bf16 sampled {seqs}")
+    ref_out, ref_lse = oracle_sampled(w, seqs)
+    out, lse = _prefill(w)
+    rows = ~np.isnan(ref_out[:, 0, 0])
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, rows=rows)
+    _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
+    assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_over_fp8_pools(gpu_lib, D):
+    ctx = [600, 1000, 129, 2048, 77, 17]
+    ql = [512, 100, 129, 64, 1, 17]
+    for name, H, KVH in [("gqa4", 32, 8), ("gqa8", 16, 2), ("mha", 4, 4)]:
+        spec = W.custom(f"pf8_{name}_{D}", ctx, q_len=ql, num_heads=H, num_kv_heads=KVH, head_dim=D, kv_fp8=True,
+                        k_scale=0.05, v_scale=0.02)
+        _check(spec, f"prefill over E4M3 pools {name} D {D}")
+
+
+def test_prefill_fp8_workload_sampled(gpu_lib):
+    w = W.build("prefill_chunk_fp8kv", DEV)
+    seqs = [1, 6, 14]
+    _say(f"[case] prefill_chunk_fp8kv sampled {seqs}")
     ref_out, ref_lse = oracle_sampled(w, seqs)
     out, lse = _prefill(w)
     rows = ~np.isnan(ref_out[:, 0, 0])
