@@ -5,8 +5,10 @@
 // decode's matrix-core page step (mfma_wave.h) on the staged pages.
 //
 // LDS layout of a page: K rows of D bf16 (one per token), each followed by PKV_LDS_KPAD bytes; V as
-// D rows of 16 tokens, each row's four 4-token groups stored in slots g ^ vswz(d) so that the dims
-// one read instruction pairs up (d and d + 8) sit in different banks.
+// D rows of 16 tokens, each row's four 4-token groups stored in slots g ^ vswz(d).  A value read
+// serves 16 lanes per LDS cycle: the 16 dims of one 4-token group, whose rows are 32 bytes apart, so
+// without the swizzle dims d, d + 4, d + 8, d + 12 would hit the same banks; XOR-ing the slot with
+// bits 2-3 of the dim puts all 16 reads in different bank pairs (and the staging writes too).
 #pragma once
 
 #include <type_traits>
@@ -19,7 +21,7 @@
 
 namespace pkv {
 
-__device__ __forceinline__ int vswz(int d) { return (d >> 3) & 3; }
+__device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
 
 template <int D, int SP>
 struct LdsPages {

@@ -10,9 +10,9 @@
 // cores to be the bound, and the K/V pages are reused by every row tile.  So:
 //  * one workgroup per (sequence, kv head, block of 128 rows); rows = new tokens x the G query heads
 //    of the kv head, in token order; each of its 4 waves owns 32 rows (two 16-row MFMA tiles), so
-//    two workgroups fit a CU (64 rows per wave, one workgroup per CU, measured slower);
-//  * every K/V page is fetched once per workgroup, staged in LDS four pages at a time (double-
-//    buffered: the next four pages' loads fly while these are computed) and read by all four waves;
+//    two or three workgroups fit a CU (64 rows per wave, one workgroup per CU, measured slower);
+//  * every K/V page is fetched once per workgroup, staged in LDS a few pages at a time (double-
+//    buffered: the next stage's loads fly while this one is computed) and read by all four waves;
 //  * a workgroup stops at the page holding its last row's last visible key (causal), and a wave
 //    skips the pages past its own rows' limit;
 //  * per page, each wave runs the decode's matrix-core step (scores, mask, online softmax, P.V);
@@ -26,8 +26,19 @@ namespace pkv {
 constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
-template <int D, int SP, bool F8>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
+// Pages per LDS stage and the waves per SIMD the register allocation aims at.  Over bf16 pools: four
+// pages, and the compiler's own choice (about 200 VGPRs at D = 128, two waves per SIMD).  Over E4M3
+// pools the staging registers hold half the bytes, so two-page stages (34 KB of LDS per workgroup)
+// and at most 168 VGPRs let three workgroups share a CU: 12% faster there.  Over bf16 pools the same
+// limit spills (2% slower), and one-page stages with it cost a barrier per page (4% slower).
+template <bool F8> struct PrefillCfg {
+  static constexpr int SP = F8 ? 2 : 4;
+  static constexpr int WAVES_PER_SIMD = F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
+};
+
+template <int D, bool F8>
+__global__ __launch_bounds__(256, PrefillCfg<F8>::WAVES_PER_SIMD) void prefill_mfma_kernel(DecodeArgs a) {
+  constexpr int SP = PrefillCfg<F8>::SP;
   constexpr int NT = kPrefillNT;
   constexpr int WROWS = 16 * NT;             // rows per wave
   __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
@@ -80,11 +91,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(DecodeArgs a) {
 hipError_t launch_prefill_mfma(const DecodeArgs &a, int head_dim, bool f8, hipStream_t st) {
   const dim3 grid((unsigned)(a.per_xcd * 8));
   if (head_dim == 64) {
-    if (f8) prefill_mfma_kernel<64, 4, true><<<grid, 256, 0, st>>>(a);
-    else prefill_mfma_kernel<64, 4, false><<<grid, 256, 0, st>>>(a);
+    if (f8) prefill_mfma_kernel<64, true><<<grid, 256, 0, st>>>(a);
+    else prefill_mfma_kernel<64, false><<<grid, 256, 0, st>>>(a);
   } else {
-    if (f8) prefill_mfma_kernel<128, 4, true><<<grid, 256, 0, st>>>(a);
-    else prefill_mfma_kernel<128, 4, false><<<grid, 256, 0, st>>>(a);
+    if (f8) prefill_mfma_kernel<128, true><<<grid, 256, 0, st>>>(a);
+    else prefill_mfma_kernel<128, false><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }
