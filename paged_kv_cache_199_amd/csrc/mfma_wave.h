@@ -87,14 +87,18 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   const int grp = lane >> 4;
-  float4_t sc[NT];
+  // x = raw score * scale - running max in one rounding: the exp2 argument.  The raw scores stay
+  // for the rare step that moves the max (the max may still be the seed, which x cannot resolve).
+  float4_t c[NT], x[NT];
   #pragma unroll
   for (int n = 0; n < NT; ++n) {
     float4_t c4 = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-    for (int c = 0; c < NK; ++c)
-      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]), w.qB[n][c], c4, 0, 0, 0);
-    sc[n] = c4 * a.scale_log2;
+    for (int k = 0; k < NK; ++k)
+      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[k]), w.qB[n][k], c4, 0, 0, 0);
+    c[n] = c4;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) x[n][e] = fmaf(c4[e], a.scale_log2, -st.m[n]);
   }
   if (!ok || bstart + kBlock > w.first_last + 1) {
     // the page reaches past some row's last visible key (causal edge or context tail)
@@ -103,7 +107,7 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si
     for (int n = 0; n < NT; ++n) {
       #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (!ok || pos0 + e > w.last[n]) sc[n][e] = -INFINITY;
+        if (!ok || pos0 + e > w.last[n]) x[n][e] = -INFINITY;
     }
     const int valid = ok ? si.ctx - bstart : 0;
     if (valid < kBlock) {
@@ -120,14 +124,16 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si
   // lazy running max: moves only when a score exceeds it by more than kRescaleSlack
   bool need = false;
   #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const float th = st.m[n] + kRescaleSlack;
-    need |= sc[n][0] > th || sc[n][1] > th || sc[n][2] > th || sc[n][3] > th;
-  }
+  for (int n = 0; n < NT; ++n)
+    need |= fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])) > kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
     #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      float bm = fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3]));
+      // masked scores are exactly -inf in x; every other x is finite
+      float4_t sc;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = x[n][e] == -INFINITY ? -INFINITY : c[n][e] * a.scale_log2;
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float mn = fmaxf(st.m[n], bm);
@@ -136,14 +142,16 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si
       st.lsum[n] *= alpha;
       #pragma unroll
       for (int t = 0; t < ND; ++t) st.acc[n][t] *= alpha;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) x[n][e] = sc[e] - mn;
     }
   }
   #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const float p0 = exp2_hw(sc[n][0] - st.m[n]);
-    const float p1 = exp2_hw(sc[n][1] - st.m[n]);
-    const float p2 = exp2_hw(sc[n][2] - st.m[n]);
-    const float p3 = exp2_hw(sc[n][3] - st.m[n]);
+    const float p0 = exp2_hw(x[n][0]);
+    const float p1 = exp2_hw(x[n][1]);
+    const float p2 = exp2_hw(x[n][2]);
+    const float p3 = exp2_hw(x[n][3]);
     st.lsum[n] += (p0 + p1) + (p2 + p3);
     const uint2 pw = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
     const short4_t pB = __builtin_bit_cast(short4_t, pw);
