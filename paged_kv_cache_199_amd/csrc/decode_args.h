@@ -40,6 +40,7 @@ struct DecodeArgs {
   int64_t spill_base;          // first spill row of part_o / part_lse; -1: no spill rows (grid)
   int share_waves;             // waves per XCD in the persistent grid
   int cut_align;               // share boundaries inside a work item fall on multiples of this
+  int item_cost;               // pages of stream charged to each work item's start (its pipeline restart)
   int rows_per_tile;
   // append in the same pass: the new tokens' K/V rows, [total_q, num_kv_heads, head_dim] packed like
   // q; NULL when nothing is appended
@@ -120,12 +121,15 @@ __device__ __forceinline__ int shared_len(const SeqInfo &si, int pg) {
   return min(pg, (si.ctx - si.qs) / 16 * 16);
 }
 
-// The balanced schedule's page stream: for each kv head, for each sequence, for each row tile, the
-// sequence's pages in logical order; kv head kvh's part starts at kvh * I (I = pages per kv head, so
-// L = I * num_kv_heads in all).  Share `ord` of the NW = 8 W waves starts at floor(L ord / NW);
-// ord = x * W + wx is wave wx of XCD x, so each XCD takes one contiguous eighth of the stream.  A
-// boundary that falls inside a work item moves down to a multiple of cut_align pages from the
-// item's start (1 when no partitions are asked for), so a share starts where its ring cycles can.
+// The balanced schedule's page stream: for each kv head, for each sequence, for each row tile, a work
+// item of C = item_cost virtual pages (the time a wave loses restarting its page pipeline on a new
+// item) followed by the sequence's pages in logical order; a sequence with no pages has empty items.
+// Kv head kvh's part starts at kvh * I (I = stream pages per kv head, so L = I * num_kv_heads in
+// all).  Share `ord` of the NW = 8 W waves starts at floor(L ord / NW); ord = x * W + wx is wave wx
+// of XCD x, so each XCD takes one contiguous eighth of the stream.  A boundary that falls in an
+// item's virtual pages moves to the item's start; one that falls on its real pages moves down to a
+// multiple of cut_align pages from the first of them (1 when no partitions are asked for), so a
+// share starts where its ring cycles can, or at an item start when that multiple is 0.
 // L ord < 2^53, so the double quotient has the exact floor: it is correctly rounded, and an integer
 // quotient is representable.
 __device__ __forceinline__ int64_t share_raw(int64_t L, int NW, int ord) {

@@ -104,17 +104,19 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, PrefixArgs p
   const int W = a.share_waves;
   const int NW = 8 * W;
   const int N = a.cut_align;                              // 1, 2 or 4
+  const int C = a.item_cost;                              // virtual pages at each item's start
   const int PP = a.part_size / kBlock;
+  int nblk = 0;
   if (spill) {
     const int G = a.group;
     const int rloc = i * G + h % G;
     const int rt = rloc / a.rows_per_tile;
     srow = rloc - rt * a.rows_per_tile;
-    const int nblk = (si.ctx + kBlock - 1) / kBlock;
+    nblk = (si.ctx + kBlock - 1) / kBlock;
     const int I = pre_all;
     L = (int64_t)I * a.num_kv_heads;
-    pos0 = (int64_t)(h / G) * I + pre_s + (int64_t)rt * nblk;
-    pos1 = pos0 + nblk;
+    pos0 = (int64_t)(h / G) * I + pre_s + (int64_t)rt * (nblk + C);
+    pos1 = pos0 + nblk + C;
     ord0 = first_share_above(L, NW, pos0);
     ncand = max(0, first_share_above(L, NW, pos1 - 1) - ord0);
   }
@@ -127,13 +129,18 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, PrefixArgs p
       return true;
     }
     const int ord = ord0 + idx - si.nparts;
+    // real page offset in the item where a raw share start lands (0: the item's start)
+    auto real_off = [&](int64_t b) {
+      const int ro = (int)(b - pos0) - C;
+      return ro > 0 ? ro & ~(N - 1) : 0;
+    };
     const int64_t b = share_raw(L, NW, ord);                // in (pos0, pos1)
-    const int ob = (int)(b - pos0) & ~(N - 1);              // rounded offset in the item
+    const int ob = real_off(b);
     if (ob <= 0) return false;
     cut = true;
     if (ob % PP == 0) return false;
     const int64_t bn = share_raw(L, NW, ord + 1);
-    const int64_t obn = bn < pos1 ? (int)(bn - pos0) & ~(N - 1) : bn - pos0;
+    const int obn = bn < pos1 ? real_off(bn) : nblk;
     if (obn <= ob) return false;
     prow = a.spill_base + (int64_t)share_slot(W, ord) * a.rows_per_tile + srow;
     return true;

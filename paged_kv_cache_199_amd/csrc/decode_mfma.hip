@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
         qraw = max(a.q_lens ? a.q_lens[s] : a.max_q_len, 0);
         qs = max(1, min(qraw, ctx));
         rt = (qs * G + ROWS - 1) / ROWS;
-        pages = (ctx + kBlock - 1) / kBlock * rt;
+        const int nb = (ctx + kBlock - 1) / kBlock;
+        pages = nb > 0 ? (nb + a.item_cost) * rt : 0;
       }
       const int inc_pages = wave_incl_scan(pages, lane);
       const int inc_q = wave_incl_scan(qraw, lane);
@@ -203,13 +204,17 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     }
     return s0;
   };
+  const int C = a.item_cost;
   auto cut = [&](int64_t b) -> int64_t {
     if (b >= L) return L;
     const int kvh = (int)(b / I);
     const int r = (int)(b - (int64_t)kvh * I);
     const int s = seq_of(r);
-    const int nblk = (tctx[s] + kBlock - 1) / kBlock;
-    return b - ((r - pre[s]) % nblk) % N;
+    const int span = (tctx[s] + kBlock - 1) / kBlock + C;
+    const int off = (r - pre[s]) % span;        // stream offset in the item
+    const int ro = off - C;                     // real page offset (<= 0: the item's virtual pages)
+    const int rr = ro > 0 ? ro - ro % N : 0;
+    return b - off + (rr > 0 ? C + rr : 0);
   };
   int64_t k = cut(share_raw(L, NW, ord));
   const int64_t k_end = cut(share_raw(L, NW, ord + 1));
@@ -229,10 +234,14 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     si.qbase = __builtin_amdgcn_readfirstlane(tqb[s]);
     si.nparts = (si.ctx + a.part_size - 1) / a.part_size;
     const int nblk = (si.ctx + kBlock - 1) / kBlock;
+    const int span = nblk + C;
     const int local = __builtin_amdgcn_readfirstlane(r - pre[s]);
-    const int rt = local / nblk;
-    const int j0 = local - rt * nblk;
+    const int rt = local / span;
+    const int off = local - rt * span;
+    const int j0 = max(off - C, 0);               // k is an item start or on a real page
+    k += j0 + C - off;                            // stream position of real page j0
     const int run = (int)min((int64_t)(nblk - j0), k_end - k);
+    if (run <= 0) break;                          // never taken: boundaries are item starts or real pages
 
     const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // appending: does this run reach the new tokens (the sequence's last qs positions)?

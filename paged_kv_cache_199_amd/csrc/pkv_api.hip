@@ -325,6 +325,13 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.share_waves = pl.grid / 8 * 4;
   // share boundaries must start ring cycles only where a partition end could fall inside a run
   a.cut_align = pl.num_parts > 1 ? pl.depth : 1;
+  // a wave that starts a work item restarts its page pipeline (new q rows, new block-table row, the
+  // first pages' full latency): charging each item 4 pages of stream evens out the waves' finish
+  // times.  Measured on conc32 / speculative verify / conc32 over E4M3 pools, step time for 0, 2, 4,
+  // 6, 8, 12: 39.6 / 38.7 / 38.6 / 38.4 / 38.3 / 39.1 us, 123.8 / 121.0 / 120.4 / 120.9 / 120.9 /
+  // 120.7 us, 34.2 / 33.2 / 32.8 / 32.7 / 32.6 / 33.7 us; long context (items of hundreds of pages)
+  // stays within 0.2% up to 4 and loses 0.3-0.5% at 6-8.
+  a.item_cost = persist ? 4 : 0;
   a.rows_per_tile = pl.rows_per_tile;
   // the persistent matrix-core kernel appends in its own pass (up to 8 new tokens per sequence);
   // every other launch appends with a small kernel first
