@@ -141,4 +141,112 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
   }
 }
 
+// bf16 pools, D = 128: the same page walk with each stage fetched by gfx950's global-to-LDS loads
+// (global_load_lds_dwordx4), so no VGPRs hold pages in flight.  Such a load writes 16 bytes per lane
+// to consecutive LDS addresses (lane l at base + 16 l); each lane picks the global 16-byte chunk
+// that belongs there.  Page layout in LDS (8 KB): K as 16 token rows of 256 bytes, chunk c of row r
+// stored at position c ^ r (the 16 rows one K read touches then fall in different banks); V as 128
+// dim rows of 32 bytes (16 tokens), the two chunks of a row swapped where bit 2 of the dim is set
+// (2-way bank conflicts on V reads, the least that 16-byte chunks allow).  Two stage buffers are
+// separate LDS arrays, and the walk alternates between them with the buffer known at compile time,
+// so the compiler sees that reads of one never wait for loads into the other.
+template <int SP>
+struct DmaPages {
+  static constexpr int D = 128;
+  static constexpr int KBYTES = kBlock * D * 2;
+  static constexpr int PBYTES = 2 * KBYTES;          // K then V
+  static constexpr int BYTES = SP * PBYTES;          // one stage buffer
+};
+
+template <int NT, int SP>
+__device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const SeqInfo &si, int kvh,
+                                                     const int32_t *bt, int jb, int je, int jw,
+                                                     char *buf0, char *buf1, const WaveRows<128, NT> &w,
+                                                     WaveAcc<128, NT> &st) {
+  typedef DmaPages<SP> L;
+  constexpr int D = 128;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int n = je - jb;
+  if (n <= 0) return;
+  const int nstages = (n + SP - 1) / SP;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  constexpr int64_t page_bytes = (int64_t)kBlock * D * 2;
+  // this lane's chunk of the 1 KB K block (rows 4 wave .. + 3) and V block (dims 32 wave .. + 31)
+  // that its wave moves for every page
+  const int kr_row = 4 * wave + (lane >> 4);
+  const int k_off = kr_row * (D * 2) + (((lane & 15) ^ kr_row) * 16);
+  const int vd = 32 * wave + (lane >> 1);
+  const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> 2) & 1)) * 16);
+  // issue stage g's loads into buffer dst; returns bit p set when page p has a valid block id
+  auto fetch = [&](int g, char *dst) -> int {
+    int okn = 0;
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = jb + min(g * SP + p, n - 1);     // past the end: re-read the last page
+      const int bid = bt[j];
+      const bool ok = bid >= 0 && bid < a.num_blocks;
+      okn |= ok ? 1 << p : 0;
+      const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
+      char *pg = dst + p * L::PBYTES;
+      __builtin_amdgcn_global_load_lds(kbase + page + k_off, (__attribute__((address_space(3))) void *)(pg + wave * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + page + v_off,
+                                       (__attribute__((address_space(3))) void *)(pg + L::KBYTES + wave * 1024), 16, 0, 0);
+    }
+    return __builtin_amdgcn_readfirstlane(okn);
+  };
+  // compute pages [p0, p1) of stage g from buffer src
+  auto compute = [&](int g, const char *src, int ok_bits, int p0, int p1) {
+    const int j0 = jb + g * SP;
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      if (p >= p0 && p < p1 && j0 + p < jw) {
+        const char *pg = src + p * L::PBYTES;
+        uint4 kr[NK];
+        uint2 vr[ND];
+        #pragma unroll
+        for (int c = 0; c < NK; ++c)
+          kr[c] = *reinterpret_cast<const uint4 *>(pg + col * (D * 2) + (((4 * c + grp) ^ col) * 16));
+        #pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          const int d = col + 16 * t;
+          vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + d * (kBlock * 2) +
+                                                   ((((grp >> 1) ^ ((d >> 2) & 1)) * 16) + (grp & 1) * 8));
+        }
+        mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
+      }
+    }
+  };
+
+  int ok0 = fetch(0, buf0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int g = 0; g < nstages; g += 2) {
+    // even stage from buf0 while the next one lands in buf1
+    // (the next stage's loads are issued after this stage's first page: at three waves per SIMD the
+    // page step spills a register whose reload waits on every load in flight, and the first page
+    // holds it)
+    int ok1 = 0;
+    compute(g, buf0, ok0, 0, 1);
+    if (g + 1 < nstages) ok1 = fetch(g + 1, buf1);
+    compute(g, buf0, ok0, 1, SP);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads into buf1 have landed
+    __syncthreads();
+    if (g + 1 >= nstages) break;
+    // odd stage from buf1 while the next one lands in buf0
+    compute(g + 1, buf1, ok1, 0, 1);
+    if (g + 2 < nstages) ok0 = fetch(g + 2, buf0);
+    compute(g + 1, buf1, ok1, 1, SP);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+}
+
 }  // namespace pkv

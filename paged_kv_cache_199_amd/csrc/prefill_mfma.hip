@@ -26,22 +26,27 @@ namespace pkv {
 constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
-// Pages per LDS stage and the waves per SIMD the register allocation aims at.  Over bf16 pools: four
-// pages, and the compiler's own choice (about 200 VGPRs at D = 128, two waves per SIMD).  Over E4M3
-// pools the staging registers hold half the bytes, so two-page stages (34 KB of LDS per workgroup)
-// and at most 168 VGPRs let three workgroups share a CU: 12% faster there.  Over bf16 pools the same
-// limit spills (2% slower), and one-page stages with it cost a barrier per page (4% slower).
-template <bool F8> struct PrefillCfg {
-  static constexpr int SP = F8 ? 2 : 4;
-  static constexpr int WAVES_PER_SIMD = F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
+// How pages reach LDS, pages per stage, and the waves per SIMD the register allocation aims at.
+//  * bf16 pools, D = 128: global-to-LDS loads (no staging registers), three-page stages (2 x 24 KB
+//    of LDS per workgroup) and at most 168 VGPRs, so three workgroups share a CU: 11% faster than
+//    staging through registers at two waves per SIMD.
+//  * E4M3 pools: pages are widened to bf16 on the way, so they pass through registers, which hold
+//    half the bytes: two-page stages (34 KB) and at most 168 VGPRs, three workgroups per CU (12%
+//    faster than two).
+//  * bf16 pools, D = 64: four-page stages through registers; the compiler's allocation already
+//    fits three waves per SIMD.
+template <int D, bool F8> struct PrefillCfg {
+  static constexpr bool DMA = !F8 && D == 128;
+  static constexpr int SP = DMA ? 3 : F8 ? 2 : 4;
+  static constexpr int WAVES_PER_SIMD = DMA || F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
 };
 
 template <int D, bool F8>
-__global__ __launch_bounds__(256, PrefillCfg<F8>::WAVES_PER_SIMD) void prefill_mfma_kernel(DecodeArgs a) {
-  constexpr int SP = PrefillCfg<F8>::SP;
+__global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void prefill_mfma_kernel(DecodeArgs a) {
+  typedef PrefillCfg<D, F8> Cfg;
+  constexpr int SP = Cfg::SP;
   constexpr int NT = kPrefillNT;
   constexpr int WROWS = 16 * NT;             // rows per wave
-  __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -83,7 +88,14 @@ __global__ __launch_bounds__(256, PrefillCfg<F8>::WAVES_PER_SIMD) void prefill_m
   init_acc<D, NT>(st);
 
   const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  lds_stream_pages<D, NT, SP, F8>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
+  if constexpr (Cfg::DMA) {
+    __shared__ __attribute__((aligned(16))) char buf0[DmaPages<SP>::BYTES];
+    __shared__ __attribute__((aligned(16))) char buf1[DmaPages<SP>::BYTES];
+    lds_stream_pages_dma<NT, SP>(a, si, kvh, bt, 0, npages, my_pages, buf0, buf1, w, st);
+  } else {
+    __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
+    lds_stream_pages<D, NT, SP, F8>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
+  }
   if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
 }
 
