@@ -92,11 +92,13 @@ def measured_traffic(workload: str, path: str, schedule: str, part_size: int, de
     return d.get("bytes_per_launch")
 
 
-def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int):
+def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int, item_cost: int = 0):
     """Per-wave K/V page lists in the order the persistent decode schedule visits them: the stream of
-    pages (kv head, sequence, row tile, logical page) kv-head-major, cut into NW equal shares (share
-    x * W + wx goes to wave wx of XCD x; workgroup i runs on XCD i % 8), each boundary that falls
-    inside a work item moved down to a multiple of cut_align pages from the item's start."""
+    work items (kv head, sequence, row tile) kv-head-major, each item_cost virtual pages followed by
+    its logical pages, cut into NW equal shares (share x * W + wx goes to wave wx of XCD x; workgroup
+    i runs on XCD i % 8).  A boundary on an item's virtual pages moves to the item's start; one on its
+    real pages moves down to a multiple of cut_align pages from the first of them.  Virtual pages
+    are dropped from the lists."""
     KVH, B = w.spec.num_kv_heads, w.spec.block_size
     G = w.spec.num_heads // KVH
     parts, starts = [], []
@@ -104,12 +106,15 @@ def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int):
     for kvh in range(KVH):
         for s in range(w.num_seqs):
             nblk = (int(w.context_lens[s]) + B - 1) // B
+            if nblk == 0:
+                continue
             row_ids = w.block_tables[s, :nblk].astype(np.int64) * KVH + kvh
             rts = -(-int(w.q_lens[s]) * G // rows_per_tile)
             for _ in range(rts):
+                parts.append(np.full(item_cost, -1, np.int64))
                 parts.append(row_ids)
                 starts.append(pos)
-                pos += nblk
+                pos += item_cost + nblk
     stream = np.concatenate(parts)
     starts = np.asarray(starts, np.int64)
     L = len(stream)
@@ -122,13 +127,16 @@ def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int):
         if b >= L:
             return L
         st = starts[np.searchsorted(starts, b, side="right") - 1]
-        return b - (b - st) % cut_align
+        ro = b - st - item_cost
+        rr = ro - ro % cut_align if ro > 0 else 0
+        return st + (item_cost + rr if rr > 0 else 0)
 
     lists = [np.zeros(0, np.int64)] * waves
     for o in range(8 * W):
         a, b = cut(raw(o)), cut(raw(o + 1))
         x, wx = divmod(o, W)
-        lists[((wx // 4) * 8 + x) * 4 + wx % 4] = stream[a:b]
+        seg = stream[a:b]
+        lists[((wx // 4) * 8 + x) * 4 + wx % 4] = seg[seg >= 0]
     return lists
 
 
@@ -141,7 +149,7 @@ def pattern_ceiling(w, plan, kcs, vcs, reps: int = 3):
     from paged_kv_cache_199_amd import _lib
 
     cut_align = plan["pipeline_depth"] if plan["num_partitions"] > 1 else 1
-    lists = decode_order_pages(w, plan["rows_per_tile"], plan["grid_waves"], cut_align)
+    lists = decode_order_pages(w, plan["rows_per_tile"], plan["grid_waves"], cut_align, plan["item_cost"])
     offs = np.zeros(len(lists) + 1, np.int64)
     offs[1:] = np.cumsum([len(l) for l in lists])
     dev = kcs[0].device

@@ -159,6 +159,9 @@ typedef struct pkv_decode_plan_info {
   int schedule;            /* PKV_SCHEDULE_GRID or PKV_SCHEDULE_PERSISTENT */
   int grid_waves;          /* persistent schedule: waves of its grid on the current device; else 0 */
   size_t workspace_bytes;  /* same value as pkv_decode_workspace_bytes() */
+  int item_cost;           /* persistent schedule: stream pages charged to each (sequence, kv head,
+                              row tile) work item's start when the page stream is cut into equal
+                              shares; else 0 */
 } pkv_decode_plan_info;
 
 /* Fills *info; returns PKV_OK or a negative pkv_status on bad sizes / options. */

@@ -34,7 +34,8 @@ class DecodeOptions(ctypes.Structure):
 class DecodePlanInfo(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("num_partitions", _c_int), ("path", _c_int),
                 ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("pipeline_depth", _c_int),
-                ("schedule", _c_int), ("grid_waves", _c_int), ("workspace_bytes", _c_sz)]
+                ("schedule", _c_int), ("grid_waves", _c_int), ("workspace_bytes", _c_sz),
+                ("item_cost", _c_int)]
 
 
 _lib: Optional[ctypes.CDLL] = None

@@ -103,11 +103,14 @@ __device__ __forceinline__ SeqInfo prefix_seq(int pg) {
 // bf16 pools.  Workgroups [0, item_wgs) run the shared pass, one per (group, kv head, chunk, block of
 // four row tiles): the chunk's pages go through LDS once for the four waves (lds_pages.h).  The
 // workgroups after them build the suffix tables.
+// D = 128: pages reach LDS through gfx950's global-to-LDS loads in two-page stages (lds_pages.h),
+// 1.6% faster on a 64-sequence, 4096-token prefix than staging through registers.  Limiting the
+// kernel to three waves per SIMD there spills and is 4-6% slower.
 template <int D>
 __global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, PrefixArgs p, int item_wgs) {
   constexpr int NT = kPrefixRows / 16;
-  constexpr int SP = 4;
-  __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
+  constexpr bool DMA = D == 128;
+  constexpr int SP = DMA ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x >= item_wgs) {
@@ -146,7 +149,14 @@ __global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, Pr
   DecodeArgs ap = a;
   ap.part_o = p.pre_o;
   ap.part_lse = p.pre_lse;
-  lds_stream_pages<D, NT, SP>(ap, prefix_seq(pg), kvh, bt_row, jb, je, jw, lds, w, st);
+  if constexpr (DMA) {
+    __shared__ __attribute__((aligned(16))) char buf0[DmaPages<SP>::BYTES];
+    __shared__ __attribute__((aligned(16))) char buf1[DmaPages<SP>::BYTES];
+    lds_stream_pages_dma<NT, SP>(ap, prefix_seq(pg), kvh, bt_row, jb, je, jw, buf0, buf1, w, st);
+  } else {
+    __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
+    lds_stream_pages<D, NT, SP>(ap, prefix_seq(pg), kvh, bt_row, jb, je, jw, lds, w, st);
+  }
   const int64_t item = (((int64_t)g * KVH + kvh) * C + c) * RT + rt;
   if (live) finish_wave<D, NT>(ap, 0, false, lane, w, st, item * kPrefixRows);
 }

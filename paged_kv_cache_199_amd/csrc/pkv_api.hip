@@ -69,6 +69,7 @@ struct Plan {
   int part_size;
   int num_parts;
   int grid;          // persistent schedule: workgroups (a multiple of 8)
+  int item_cost;     // persistent schedule: pages of stream charged to each work item's start
   int64_t part_rows; // partial rows: num_parts * total_q * num_heads, plus the spill rows
   int64_t spill_base;
   bool need_q_start;
@@ -132,6 +133,13 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   const bool can_persist = pl.path == PKV_PATH_MFMA && num_seqs <= pkv::persistent_max_seqs() &&
                            stream_pages * num_kv_heads < ((int64_t)1 << 31);
   pl.schedule = (asked_sched == PKV_SCHEDULE_GRID || !can_persist) ? PKV_SCHEDULE_GRID : PKV_SCHEDULE_PERSISTENT;
+  // a wave that starts a work item restarts its page pipeline (new q rows, new block-table row, the
+  // first pages' full latency): charging each item 4 pages of stream evens out the waves' finish
+  // times.  Measured on conc32 / speculative verify / conc32 over E4M3 pools, step time for 0, 2, 4,
+  // 6, 8, 12: 39.6 / 38.7 / 38.6 / 38.4 / 38.3 / 39.1 us, 123.8 / 121.0 / 120.4 / 120.9 / 120.9 /
+  // 120.7 us, 34.2 / 33.2 / 32.8 / 32.7 / 32.6 / 33.7 us; long context (items of hundreds of pages)
+  // stays within 0.2% up to 4 and loses 0.3-0.5% at 6-8.
+  pl.item_cost = pl.schedule == PKV_SCHEDULE_PERSISTENT ? 4 : 0;
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
   pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth
                                             : pkv::mfma_default_depth(head_dim, R, persist);
@@ -269,6 +277,7 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   info->grid_waves = pl.grid * 4;
   info->schedule = pl.schedule;
   info->workspace_bytes = pl.bytes;
+  info->item_cost = pl.item_cost;
   return PKV_OK;
 }
 
@@ -325,13 +334,7 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.share_waves = pl.grid / 8 * 4;
   // share boundaries must start ring cycles only where a partition end could fall inside a run
   a.cut_align = pl.num_parts > 1 ? pl.depth : 1;
-  // a wave that starts a work item restarts its page pipeline (new q rows, new block-table row, the
-  // first pages' full latency): charging each item 4 pages of stream evens out the waves' finish
-  // times.  Measured on conc32 / speculative verify / conc32 over E4M3 pools, step time for 0, 2, 4,
-  // 6, 8, 12: 39.6 / 38.7 / 38.6 / 38.4 / 38.3 / 39.1 us, 123.8 / 121.0 / 120.4 / 120.9 / 120.9 /
-  // 120.7 us, 34.2 / 33.2 / 32.8 / 32.7 / 32.6 / 33.7 us; long context (items of hundreds of pages)
-  // stays within 0.2% up to 4 and loses 0.3-0.5% at 6-8.
-  a.item_cost = persist ? 4 : 0;
+  a.item_cost = pl.item_cost;
   a.rows_per_tile = pl.rows_per_tile;
   // the persistent matrix-core kernel appends in its own pass (up to 8 new tokens per sequence);
   // every other launch appends with a small kernel first

@@ -58,3 +58,27 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_probe_page_lists_cover_every_page_once():
+    """The page-stream probe's per-wave lists (the decode schedule's order) hold every (page, kv head,
+    row tile) a decode reads exactly once, with and without the per-item start cost and with a cut
+    alignment, for batches whose items are longer and shorter than a wave's share."""
+    spec = W.custom("order", [1, 17, 300, 1100, 2048, 5, 33], q_len=[1, 2, 5, 1, 3, 1, 1], num_heads=8,
+                    num_kv_heads=2, head_dim=64)
+    w = W.build(spec, "cpu")
+    KVH, G = 2, 4
+    for rpt in (16, 32):
+        want = []
+        for kvh in range(KVH):
+            for s in range(w.num_seqs):
+                nblk = (int(w.context_lens[s]) + 15) // 16
+                rts = -(-int(w.q_lens[s]) * G // rpt)
+                want += [int(b) * KVH + kvh for b in w.block_tables[s, :nblk]] * rts
+        for waves in (64, 1024):
+            for cost in (0, 4):
+                for align in (1, 2):
+                    lists = bench.decode_order_pages(w, rpt, waves, align, cost)
+                    assert len(lists) == waves
+                    got = np.sort(np.concatenate(lists))
+                    assert np.array_equal(got, np.sort(np.asarray(want, np.int64)))
