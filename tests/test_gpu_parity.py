@@ -145,6 +145,22 @@ def test_balanced_split_many_short_sequences(gpu_lib):
         _check_persistent(w, 0, depth)
 
 
+def test_grouped_merge_with_heavily_cut_rows(gpu_lib):
+    """4096 output rows (64 sequences x 64 heads, GQA 8, no fixed partitions): the split-K merge takes
+    the 8 heads of a kv head per wave.  One 32768-token sequence among short ones is cut into more
+    pieces than that merge holds, so its rows go through the per-row merge inside the same launch;
+    the other rows have a few pieces or none."""
+    rng = np.random.default_rng(17)
+    ctx = [32768] + rng.integers(16, 400, 63).tolist()
+    spec = W.custom("grouped_merge", ctx, num_heads=64, num_kv_heads=8, head_dim=128)
+    w = W.build(spec, DEV)
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, 1, w.max_context_len, 64, 8, 128, _lib.PKV_BF16, path=_lib.PATH_MFMA,
+                            schedule=_lib.SCHEDULE_PERSISTENT)
+    assert plan["num_partitions"] == 1 and plan["schedule"] == _lib.SCHEDULE_PERSISTENT
+    for depth in (2, 4):
+        _check_persistent(w, 0, depth)
+
+
 @pytest.mark.parametrize("S", [4096, 4100])
 def test_largest_batch_the_persistent_schedule_lists(gpu_lib, S):
     """4096 sequences: the persistent kernel's LDS tables at their largest (the library's limit);
