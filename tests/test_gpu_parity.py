@@ -161,6 +161,20 @@ def test_grouped_merge_with_heavily_cut_rows(gpu_lib):
         _check_persistent(w, 0, depth)
 
 
+@pytest.mark.parametrize("H,KVH,D,q", [(16, 8, 128, 1), (64, 8, 64, 1), (64, 4, 64, 2)])
+def test_grouped_merge_head_layouts(gpu_lib, H, KVH, D, q):
+    """The grouped merge's other lane layouts (G x D / 64 floats per lane): G = 8 and G = 16 at D = 64,
+    G = 2 at D = 128, each with at least 4096 rows and ragged contexts, so rows have 1..several
+    pieces."""
+    rng = np.random.default_rng(H * 100 + D + q)
+    S = max(16, -(-4096 // (H * q)))
+    ctx = rng.integers(q, 700, S).tolist()
+    spec = W.custom(f"grouped_{H}_{KVH}_{D}_{q}", ctx, q_len=q, num_heads=H, num_kv_heads=KVH, head_dim=D)
+    w = W.build(spec, DEV)
+    assert w.total_q * H >= 4096
+    _check_persistent(w, 0, 2)
+
+
 @pytest.mark.parametrize("S", [4096, 4100])
 def test_largest_batch_the_persistent_schedule_lists(gpu_lib, S):
     """4096 sequences: the persistent kernel's LDS tables at their largest (the library's limit);
