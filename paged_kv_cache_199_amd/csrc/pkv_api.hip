@@ -433,10 +433,11 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
 namespace {
 
 // Read-once shared-prefix decode: workspace carving and the chunking of the prefix pass.
-// Bytes the read-once pass must save before it pays: measured crossover over groups of 4..64
-// sequences sharing 512..4096 tokens (GQA 4, D 128) lies between 250 and 500 MiB, because the
-// per-sequence decode reads the shared pages from the Infinity Cache after the first sequence.
-constexpr int64_t kReadOnceBytes = 448ll << 20;
+// Bytes the read-once pass must save before it pays: over groups of 16..64 sequences sharing
+// 1024..4096 tokens (GQA 4, D 128) the per-sequence / read-once time ratio is 0.91-1.01 at 240-252
+// MiB saved and 1.18-1.30 at about 500 MiB (break-even near 250-340 MiB), because the per-sequence
+// decode reads the shared pages from the Infinity Cache after the first sequence.
+constexpr int64_t kReadOnceBytes = 320ll << 20;
 struct PrefixPlan {
   int rows_max, row_tiles, chunk_pages, chunks, sfx_stride;
   int64_t items;
