@@ -103,14 +103,15 @@ __device__ __forceinline__ SeqInfo prefix_seq(int pg) {
 // bf16 pools.  Workgroups [0, item_wgs) run the shared pass, one per (group, kv head, chunk, block of
 // four row tiles): the chunk's pages go through LDS once for the four waves (lds_pages.h).  The
 // workgroups after them build the suffix tables.
-// D = 128: pages reach LDS through gfx950's global-to-LDS loads in two-page stages (lds_pages.h),
-// 1.6% faster on a 64-sequence, 4096-token prefix than staging through registers.  Limiting the
-// kernel to three waves per SIMD there spills and is 4-6% slower.
+// D = 128: pages reach LDS through gfx950's global-to-LDS loads (lds_pages.h), faster on a
+// 64-sequence, 4096-token prefix than staging through registers (2-page stages: 1.6%; 4-page stages
+// at one workgroup per CU: 66.5 -> 65.3 us more).  Limiting the kernel to three waves per SIMD there
+// spills and is 4-6% slower.
 template <int D>
 __global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, PrefixArgs p, int item_wgs) {
   constexpr int NT = kPrefixRows / 16;
   constexpr bool DMA = D == 128;
-  constexpr int SP = DMA ? 2 : 4;
+  constexpr int SP = 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   if ((int)blockIdx.x >= item_wgs) {
