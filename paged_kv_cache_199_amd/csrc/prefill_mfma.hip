@@ -17,8 +17,8 @@
 //    skips the pages past its own rows' limit;
 //  * per page, each wave runs the decode's matrix-core step (scores, mask, online softmax, P.V);
 //    rows end with their final output and natural-log LSE (no split: there are enough workgroups).
-// Work units are laid out row block fastest and spread over the XCDs in contiguous ranges, so the
-// workgroups that read one (sequence, kv head)'s pages share an L2.
+// Work units are laid out row block fastest (last row block first) and spread over the XCDs in
+// contiguous ranges, so the workgroups that read one (sequence, kv head)'s pages share an L2.
 #include "lds_pages.h"
 
 namespace pkv {
@@ -56,7 +56,10 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
 
   int u = xcd_unit(blockIdx.x, a.per_xcd);
   if (u >= a.units) return;
-  const int rb = u % a.row_tiles;
+  // row blocks in descending order: under the causal limit the last ones read the most pages, and
+  // dispatching them first shortens the kernel's tail (bf16 pools 445 -> 437 us, E4M3 447 -> 429 us
+  // on the chunked-prefill batch)
+  const int rb = a.row_tiles - 1 - u % a.row_tiles;
   u /= a.row_tiles;
   const int kvh = u % a.num_kv_heads;
   const int s = u / a.num_kv_heads;
