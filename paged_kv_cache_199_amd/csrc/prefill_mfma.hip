@@ -17,8 +17,9 @@
 //    skips the pages past its own rows' limit;
 //  * per page, each wave runs the decode's matrix-core step (scores, mask, online softmax, P.V);
 //    rows end with their final output and natural-log LSE (no split: there are enough workgroups).
-// Work units are laid out row block fastest (last row block first) and spread over the XCDs in
-// contiguous ranges, so the workgroups that read one (sequence, kv head)'s pages share an L2.
+// Work units are laid out row block fastest (last row block first), then sequence, then kv head, and
+// spread over the XCDs in contiguous ranges: the workgroups that read one (sequence, kv head)'s pages
+// share an L2, and every XCD gets the same kv heads' worth of work.
 #include "lds_pages.h"
 
 namespace pkv {
@@ -61,8 +62,12 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
   // on the chunked-prefill batch)
   const int rb = a.row_tiles - 1 - u % a.row_tiles;
   u /= a.row_tiles;
-  const int kvh = u % a.num_kv_heads;
-  const int s = u / a.num_kv_heads;
+  // kv head slowest: each XCD's contiguous range of units then holds whole kv heads across all the
+  // sequences (with 8 kv heads, exactly one each), so the XCDs get equal work whatever the mix of
+  // context lengths.  Sequence-major, each XCD got two whole sequences of the chunked-prefill batch,
+  // the busiest 1.57x the mean, and the kernel waited for it (436 -> 310 us).
+  const int s = u % a.num_seqs;
+  const int kvh = u / a.num_seqs;
 
   // q rows before sequence s (the workgroup sums q_lens itself: no workspace)
   SeqInfo si = load_seq(a, s);
