@@ -114,8 +114,11 @@ __global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, Pr
   constexpr int SP = 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  if ((int)blockIdx.x >= item_wgs) {
-    prefix_prep(a, p, ((int)blockIdx.x - item_wgs) * 4 + wave, lane);
+  // the shared-pass workgroups are padded to a multiple of 8 and spread over the XCDs in contiguous
+  // ranges (xcd_unit), so the row blocks of one chunk, which read the same pages, share an L2
+  const int per_xcd = (item_wgs + 7) / 8;
+  if ((int)blockIdx.x >= 8 * per_xcd) {
+    prefix_prep(a, p, ((int)blockIdx.x - 8 * per_xcd) * 4 + wave, lane);
     return;
   }
   const int RT = p.row_tiles;
@@ -123,7 +126,8 @@ __global__ __launch_bounds__(256) void prefix_attend_lds_kernel(DecodeArgs a, Pr
   const int C = p.chunks;
   const int KVH = a.num_kv_heads;
   // workgroup = ((g * KVH + kvh) * C + c) * RB + rb: the row blocks of one chunk are neighbours
-  const int wi = blockIdx.x;
+  const int wi = xcd_unit(blockIdx.x, per_xcd);
+  if (wi >= item_wgs) return;
   const int rb = wi % RB;
   const int c = (wi / RB) % C;
   const int kvh = (wi / (RB * C)) % KVH;
@@ -210,13 +214,15 @@ hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int he
   const int64_t tiles = p.chunks > 0 ? (int64_t)p.num_groups * a.num_kv_heads * p.chunks : 0;
   // bf16: a workgroup per four row tiles; E4M3: a wave per row tile
   const int item_wgs = (int)(f8 ? (tiles * p.row_tiles + 3) / 4 : tiles * ((p.row_tiles + 3) / 4));
-  const dim3 grid((unsigned)(item_wgs + (a.num_seqs + 3) / 4));
+  const int prep_wgs = (a.num_seqs + 3) / 4;
+  const dim3 grid((unsigned)(item_wgs + prep_wgs));
+  const dim3 grid_lds((unsigned)(8 * ((item_wgs + 7) / 8) + prep_wgs));   // shared pass padded for xcd_unit
   if (head_dim == 64) {
     if (f8) prefix_attend_f8_kernel<64, 2><<<grid, 256, 0, st>>>(a, p, item_wgs);
-    else prefix_attend_lds_kernel<64><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    else prefix_attend_lds_kernel<64><<<grid_lds, 256, 0, st>>>(a, p, item_wgs);
   } else {
     if (f8) prefix_attend_f8_kernel<128, 2><<<grid, 256, 0, st>>>(a, p, item_wgs);
-    else prefix_attend_lds_kernel<128><<<grid, 256, 0, st>>>(a, p, item_wgs);
+    else prefix_attend_lds_kernel<128><<<grid_lds, 256, 0, st>>>(a, p, item_wgs);
   }
   return hipGetLastError();
 }
