@@ -42,6 +42,27 @@ template <int D, bool F8> struct PrefillCfg {
   static constexpr int WAVES_PER_SIMD = DMA || F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
 };
 
+// The sequence at position k when the batch is ordered by work, largest first (context length x new
+// tokens; ties by index), for batches of up to 64 sequences; else sequence k.  Every wave computes it
+// alone: lane t holds sequence t's key and counts the keys that sort before it.
+__device__ __forceinline__ int longest_first(const DecodeArgs &a, int k, int lane) {
+  const int S = a.num_seqs;
+  if (S > 64) return k;
+  float key = -1.f;
+  if (lane < S) {
+    const int ctx = max(min(a.context_lens[lane], a.max_context_len), 0);
+    const int q = a.q_lens ? max(a.q_lens[lane], 1) : a.max_q_len;
+    key = (float)ctx * (float)q;
+  }
+  int rank = 0;
+  for (int t = 0; t < S; ++t) {
+    const float kt = __shfl(key, t);
+    rank += (kt > key || (kt == key && t < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < S && rank == k);
+  return hit ? (int)__builtin_ctzll(hit) : k;
+}
+
 template <int D, bool F8>
 __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void prefill_mfma_kernel(DecodeArgs a) {
   typedef PrefillCfg<D, F8> Cfg;
@@ -66,8 +87,11 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
   // sequences (with 8 kv heads, exactly one each), so the XCDs get equal work whatever the mix of
   // context lengths.  Sequence-major, each XCD got two whole sequences of the chunked-prefill batch,
   // the busiest 1.57x the mean, and the kernel waited for it (436 -> 310 us).
-  const int s = u % a.num_seqs;
   const int kvh = u / a.num_seqs;
+  // within the kv head, sequences in decreasing order of work: the longest workgroups start first and
+  // the dispatch tail is short (a list-scheduling model of the chunked-prefill batch: makespan 1.20x
+  // the ideal in index order, 1.10x longest first; measured 305 -> 297 us, E4M3 pools 303 -> 283 us)
+  const int s = longest_first(a, u % a.num_seqs, lane);
 
   // q rows before sequence s (the workgroup sums q_lens itself: no workspace)
   SeqInfo si = load_seq(a, s);
