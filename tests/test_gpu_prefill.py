@@ -48,6 +48,17 @@ def test_prompt_prefill_ragged(gpu_lib):
     _check(W.custom("prompt", ctx, q_len=ctx, num_heads=32, num_kv_heads=8, head_dim=128), "prompt prefill GQA 4")
 
 
+def test_prompt_prefill_batch_order(gpu_lib):
+    # the kernel starts each kv head's sequences in decreasing order of work (ranked on the GPU for up
+    # to 64 sequences, index order beyond): 64 and 70 ragged prompts with equal-work ties
+    rng = np.random.default_rng(64)
+    for S in (64, 70):
+        ctx = rng.integers(1, 120, S).tolist()
+        ctx[3] = ctx[5] = ctx[9] = 48                               # ties break by index
+        _check(W.custom(f"batch{S}", ctx, q_len=ctx, num_heads=32, num_kv_heads=8, head_dim=128),
+               f"{S} prompts GQA 4")
+
+
 def test_chunked_prefill_over_cached_context(gpu_lib):
     ctx = [600, 1000, 129, 2048, 77]
     ql = [512, 100, 129, 64, 1]
