@@ -78,7 +78,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, path: str, schedule: str, part_size: int, depth: int):
+def measured_traffic(workload: str, path: str, schedule: str, part_size: int, depth: int, grid_waves: int):
     """HBM bytes per launch of the partition kernel from committed rocprofv3 counter runs, or None when
     the kernels or the launch configuration changed since they were taken."""
     f = os.path.join(PROFILES, f"traffic_{path}_{schedule}_{workload}.json")
@@ -88,6 +88,8 @@ def measured_traffic(workload: str, path: str, schedule: str, part_size: int, de
     if d.get("source_hash") != kernel_source_hash():
         return None
     if d.get("partition_size") != part_size or d.get("pipeline_depth") != depth:
+        return None
+    if d.get("grid_waves") != grid_waves:
         return None
     return d.get("bytes_per_launch")
 
@@ -618,7 +620,7 @@ def main():
     achieved = dec_bytes / (k_ms * 1e-3) / 1e9
     sched_name = ["", "grid", "persistent"][plan["schedule"]]
     traffic = None if prefix_call else measured_traffic(spec.name, kernel.split("_")[1], sched_name, P_used,
-                                                       plan["pipeline_depth"])
+                                                       plan["pipeline_depth"], plan["grid_waves"])
     res = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + attended tokens/s, 1 GPU",
         "value": round(value, 2),

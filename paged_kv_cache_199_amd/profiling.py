@@ -93,6 +93,7 @@ def write_traffic(bench_log, fetch_dir, write_dir, copy_fetch_dir, copy_write_di
     d = {
         "workload": workload, "path": path, "schedule": schedule, "kernel": b["roofline"]["kernel"],
         "partition_size": cfg["partition_size"], "pipeline_depth": cfg["pipeline_depth"],
+        "grid_waves": cfg["grid_waves"],
         "algorithmic_bytes_per_launch": b["roofline"]["algorithmic_bytes_per_launch"],
         "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
         "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
