@@ -204,6 +204,19 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     }
     return s0;
   };
+  // the same for a wave-uniform r with all lanes active, in two dependent LDS reads: lanes compare
+  // every chunk's first entry (chunks of ceil(S / 64) <= 64 sequences), then the chunk's entries
+  // (pre is nondecreasing, so the lanes that pass form a prefix)
+  auto seq_of_wave = [&](int r) {
+    int c0 = 0, len = S;
+    if (S > 64) {
+      len = (S + 63) >> 6;
+      const int idx = lane * len;
+      c0 = (__popcll(__builtin_amdgcn_ballot_w64(idx < S && pre[idx] <= r)) - 1) * len;
+    }
+    const int idx = c0 + lane;
+    return c0 + __popcll(__builtin_amdgcn_ballot_w64(lane < len && idx < S && pre[idx] <= r)) - 1;
+  };
   const int C = a.item_cost;
   auto cut = [&](int64_t b) -> int64_t {
     if (b >= L) return L;
@@ -216,8 +229,13 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     const int rr = ro > 0 ? ro - ro % N : 0;
     return b - off + (rr > 0 ? C + rr : 0);
   };
-  int64_t k = cut(share_raw(L, NW, ord));
-  const int64_t k_end = cut(share_raw(L, NW, ord + 1));
+  // both ends of the share at once, in lanes 0 and 1 (the wave's start-up is a chain of dependent
+  // arithmetic and LDS reads at one wave per SIMD)
+  const int64_t kb = cut(share_raw(L, NW, ord + (lane & 1)));
+  const int kb_lo = (int)(uint32_t)kb, kb_hi = (int)(kb >> 32);
+  int64_t k = ((int64_t)__builtin_amdgcn_readlane(kb_hi, 0) << 32) | (uint32_t)__builtin_amdgcn_readlane(kb_lo, 0);
+  const int64_t k_end =
+      ((int64_t)__builtin_amdgcn_readlane(kb_hi, 1) << 32) | (uint32_t)__builtin_amdgcn_readlane(kb_lo, 1);
   // The share walks its work items in stream order.  A piece that covers a whole item of a sequence
   // with one partition is final; any other piece leaves a partial: the row of its partition when it
   // starts a partition, else (only the share's first piece can start inside one) this wave's spill
@@ -227,7 +245,7 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     const int r = (int)(k - (int64_t)kvh * I);
     // LDS reads come back in vector registers; the values are wave-uniform, and saying so keeps the
     // block-table row pointer scalar (its page ids then come through the scalar cache)
-    const int s = __builtin_amdgcn_readfirstlane(seq_of(r));
+    const int s = __builtin_amdgcn_readfirstlane(seq_of_wave(r));
     SeqInfo si;
     si.ctx = __builtin_amdgcn_readfirstlane(tctx[s]);
     si.qs = __builtin_amdgcn_readfirstlane(tqs[s]);
