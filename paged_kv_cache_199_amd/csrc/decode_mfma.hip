@@ -194,19 +194,10 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
   const int64_t spill_row0 = a.spill_base + (int64_t)(blockIdx.x * 4 + wave) * ROWS;
   const int PP = a.part_size / kBlock;
 
-  // sequence holding stream offset r of one kv head: the last s with pre[s] <= r (never an empty one)
-  auto seq_of = [&](int r) {
-    int s0 = 0, s1 = S;
-    while (s1 - s0 > 1) {
-      const int mid = (s0 + s1) >> 1;
-      if (pre[mid] <= r) s0 = mid;
-      else s1 = mid;
-    }
-    return s0;
-  };
-  // the same for a wave-uniform r with all lanes active, in two dependent LDS reads: lanes compare
-  // every chunk's first entry (chunks of ceil(S / 64) <= 64 sequences), then the chunk's entries
-  // (pre is nondecreasing, so the lanes that pass form a prefix)
+  // Sequence holding stream offset r of one kv head: the last s with pre[s] <= r (never an empty
+  // one).  r is wave-uniform and all lanes are active; two dependent LDS reads: lanes compare every
+  // chunk's first entry (chunks of ceil(S / 64) <= 64 sequences), then the chunk's entries (pre is
+  // nondecreasing, so the lanes that pass form a prefix).
   auto seq_of_wave = [&](int r) {
     int c0 = 0, len = S;
     if (S > 64) {
@@ -218,20 +209,25 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     return c0 + __popcll(__builtin_amdgcn_ballot_w64(lane < len && idx < S && pre[idx] <= r)) - 1;
   };
   const int C = a.item_cost;
-  auto cut = [&](int64_t b) -> int64_t {
-    if (b >= L) return L;
-    const int kvh = (int)(b / I);
-    const int r = (int)(b - (int64_t)kvh * I);
-    const int s = seq_of(r);
+  // Both ends of the share at once: lane 0 cuts share ord's raw start, lane 1 share ord + 1's (the
+  // wave's start-up is a chain of dependent arithmetic and LDS reads at one wave per SIMD, with HBM
+  // idle).  A raw start in an item's virtual pages moves to the item's start; one on its real pages
+  // moves down to a multiple of N pages from the first of them.
+  int64_t kb = L;
+  if (L > 0) {
+    const int64_t b = share_raw(L, NW, ord + (lane & 1));
+    const int64_t bc = b < L ? b : L - 1;
+    const int kvh = (int)(bc / I);
+    const int r = (int)(bc - (int64_t)kvh * I);
+    const int s0 = seq_of_wave(__builtin_amdgcn_readlane(r, 0));
+    const int s1 = seq_of_wave(__builtin_amdgcn_readlane(r, 1));
+    const int s = (lane & 1) ? s1 : s0;
     const int span = (tctx[s] + kBlock - 1) / kBlock + C;
     const int off = (r - pre[s]) % span;        // stream offset in the item
     const int ro = off - C;                     // real page offset (<= 0: the item's virtual pages)
     const int rr = ro > 0 ? ro - ro % N : 0;
-    return b - off + (rr > 0 ? C + rr : 0);
-  };
-  // both ends of the share at once, in lanes 0 and 1 (the wave's start-up is a chain of dependent
-  // arithmetic and LDS reads at one wave per SIMD)
-  const int64_t kb = cut(share_raw(L, NW, ord + (lane & 1)));
+    if (b < L) kb = bc - off + (rr > 0 ? C + rr : 0);
+  }
   const int kb_lo = (int)(uint32_t)kb, kb_hi = (int)(kb >> 32);
   int64_t k = ((int64_t)__builtin_amdgcn_readlane(kb_hi, 0) << 32) | (uint32_t)__builtin_amdgcn_readlane(kb_lo, 0);
   const int64_t k_end =
