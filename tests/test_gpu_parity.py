@@ -194,6 +194,28 @@ def test_largest_batch_the_persistent_schedule_lists(gpu_lib, S):
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
 
+@pytest.mark.parametrize("S", [63, 64, 65, 129, 200])
+def test_balanced_schedule_sequence_lookup_across_chunks(gpu_lib, S):
+    """Batches around 64 sequences: every wave finds the sequence that holds its share's ends by
+    comparing the stream table 64 entries at a time (first each chunk's first entry when there are
+    more than 64 sequences), so shares that start in the first, a middle or the last chunk, and on
+    chunk edges, must all land on the right sequence.  Ragged contexts from 1 to 700 tokens, so most
+    sequences are cut between several waves."""
+    rng = np.random.default_rng(1000 + S)
+    ctx = rng.integers(1, 701, S)
+    ctx[rng.choice(S, max(1, S // 8), replace=False)] = rng.integers(1, 17, max(1, S // 8))   # one-page items
+    spec = W.custom(f"lookup{S}", ctx.tolist(), num_heads=8, num_kv_heads=2, head_dim=128)
+    w = W.build(spec, DEV)
+    plan = _lib.decode_plan(S, w.total_q, 1, w.max_context_len, 8, 2, 128, _lib.PKV_BF16)
+    assert plan["schedule"] == _lib.SCHEDULE_PERSISTENT
+    _say(f"[case] {S} sequences, persistent schedule, {int(ctx.sum())} context tokens")
+    out, lse = run_library(w, DEV)
+    ref_out, ref_lse = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
+    assert d_out <= BF16_TOL and d_lse <= LSE_TOL
+
+
 def test_balanced_split_several_row_tiles(gpu_lib):
     """96 query rows per kv head (GQA 32, 3 new tokens): three 32-row tiles, each its own work item."""
     spec = W.custom("row_tiles", [700, 40, 2000, 3], q_len=3, num_heads=64, num_kv_heads=2, head_dim=128)
