@@ -142,6 +142,48 @@ def decode_order_pages(w, rows_per_tile: int, waves: int, cut_align: int, item_c
     return lists
 
 
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_199_amd", "libpkv_probe.so")
+_probe = None
+
+
+def probe_lib():
+    """libpkv_probe.so (include/pkv_probe.h), the page-stream probe built beside libpkv.so."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build it with `python -m paged_kv_cache_199_amd.build`")
+        lib = ctypes.CDLL(PROBE_LIB)
+        vp = ctypes.c_void_p
+        lib.pkv_probe_page_stream.restype = ctypes.c_int
+        lib.pkv_probe_page_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int,
+                                              vp, vp]
+        _probe = lib
+    return _probe
+
+
+def probe_page_stream(k_cache, v_cache, page_index, wave_offsets, sink, stream=None) -> None:
+    """Stream the listed K/V pages with the decode kernel's load shapes and no arithmetic.
+    page_index / wave_offsets: int32 on the GPU."""
+    import torch
+
+    nb, kvh, B, D = k_cache.shape
+    if not (page_index.dtype == torch.int32 and wave_offsets.dtype == torch.int32):
+        raise ValueError("int32 lists")
+    if not (k_cache.dtype in (torch.bfloat16, torch.uint8) and v_cache.dtype == k_cache.dtype
+            and v_cache.numel() == k_cache.numel() and B == 16):
+        raise ValueError("bf16 or uint8 (E4M3) pools of one shape")
+    for t in (k_cache, v_cache, page_index, wave_offsets, sink):
+        if not (t.is_cuda and t.device == k_cache.device and t.is_contiguous()):
+            raise ValueError("contiguous tensors on the pools' GPU")
+    s = torch.cuda.current_stream() if stream is None else stream
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = probe_lib().pkv_probe_page_stream(p(k_cache), p(v_cache), nb * kvh, D, k_cache.element_size(), p(page_index),
+                                           p(wave_offsets), wave_offsets.numel() - 1, p(sink),
+                                           ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"pkv_probe_page_stream failed (status {rc})")
+
+
 def pattern_ceiling(w, plan, kcs, vcs, reps: int = 3):
     """Time the page-stream probe (same loads as the decode kernel, no arithmetic) on this workload's
     pages in the decode schedule's order, rotating over the same pool copies as the timed steps.
@@ -160,13 +202,13 @@ def pattern_ceiling(w, plan, kcs, vcs, reps: int = 3):
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     R = len(kcs)
     for r in range(R):
-        _lib.probe_page_stream(kcs[r], vcs[r], flat, off_t, sink)
+        probe_page_stream(kcs[r], vcs[r], flat, off_t, sink)
     torch.cuda.synchronize()
     n = reps * R
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(n):
-        _lib.probe_page_stream(kcs[i % R], vcs[i % R], flat, off_t, sink)
+        probe_page_stream(kcs[i % R], vcs[i % R], flat, off_t, sink)
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e-3 / n, int(offs[-1])

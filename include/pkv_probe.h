@@ -1,8 +1,9 @@
 /*
- * pkv_probe.h — measurement helper of libpkv.so: how fast the memory system streams a given list of
- * KV pages with the exact load shapes the decode kernels use, with no arithmetic on the data.  The
- * benchmark runs it on the decode workload's own pages to report a memory ceiling for that access
- * pattern next to the HBM datasheet peak.  It computes nothing of the attention method.
+ * pkv_probe.h — the benchmark's measurement helper, built as its own library (libpkv_probe.so, not
+ * part of libpkv.so): how fast the memory system streams a given list of KV pages with the exact load
+ * shapes the decode kernels use, with no arithmetic on the data.  The benchmark runs it on the decode
+ * workload's own pages to report a memory ceiling for that access pattern next to the HBM datasheet
+ * peak.  It computes nothing of the attention method.
  */
 #ifndef PKV_PROBE_H
 #define PKV_PROBE_H

@@ -54,7 +54,6 @@ EXPORTS = {
                                               ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
     "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
                                         _vp]),
-    "pkv_probe_page_stream": (_c_int, [_vp, _vp, _c_i64, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp]),
     "pkv_decode_shared_prefix_workspace_bytes": (_c_sz, [_c_int] * 11 + [ctypes.POINTER(DecodeOptions)]),
     "pkv_paged_attn_decode_shared_prefix": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
@@ -123,7 +122,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _decode_code(q, k_cache, v_cache, out) -> int:
     """dtype code of a decode call: all fp32, all bf16, or bf16 q/out over uint8 E4M3 pools."""
     for t in (q, k_cache, v_cache, out):
-        _need(t.is_contiguous() and t.is_cuda, "q, caches and out: contiguous, on the GPU")
+        _need(t.is_contiguous(), "q, caches and out: contiguous")
     _need(out.dtype == q.dtype and k_cache.dtype == v_cache.dtype, "out matches q, V pool matches K pool")
     if q.dtype == torch.bfloat16 and k_cache.dtype == torch.uint8:
         return PKV_BF16_FP8KV
@@ -138,6 +137,62 @@ def _ptr(t: Optional[torch.Tensor]):
 def _need(cond: bool, msg: str):
     if not cond:
         raise ValueError(msg)
+
+
+# Device type the kernels run on (torch names ROCm devices "cuda").
+_GPU_TYPE = "cuda"
+
+
+def _on_gpu_like(ref: torch.Tensor, what: str, *tensors) -> None:
+    """Every given tensor (None skipped) lives on ref's device, and that device is a GPU: a host pointer
+    handed to a kernel would fault the GPU, so this is checked before any call."""
+    _need(ref.device.type == _GPU_TYPE, f"{what}: tensors must be on the GPU")
+    for t in tensors:
+        if t is not None:
+            _need(t.device == ref.device, f"{what}: every tensor must be on {ref.device} (got {t.device})")
+
+
+def _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, num_heads,
+                       num_kv_heads, head_dim, block_size):
+    """Shape, dtype, layout and device checks shared by the decode, prefill and shared-prefix calls.
+    Returns (total_q, num_seqs, num_blocks, dtype code)."""
+    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
+    total_q = q.shape[0]
+    S = context_lens.numel()
+    NB = k_cache.shape[0]
+    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
+    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
+          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
+    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
+    if q_lens is not None:
+        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
+              "lse: fp32 [total_q, H]")
+    _on_gpu_like(q, "decode arguments", k_cache, v_cache, block_tables, context_lens, q_lens, out, lse)
+    code = _decode_code(q, k_cache, v_cache, out)
+    return total_q, S, NB, code
+
+
+def _check_workspace(ws, q) -> int:
+    """Bytes of a caller-supplied workspace (contiguous, on q's device); 0 when None."""
+    if ws is None:
+        return 0
+    _need(ws.is_contiguous(), "workspace must be contiguous")
+    _on_gpu_like(q, "workspace", ws)
+    return ws.numel() * ws.element_size()
+
+
+def _workspace_for(nbytes: int, device, stream):
+    """A workspace the call allocates itself.  Allocated from `stream`'s pool when a stream is given, so
+    the caching allocator does not hand the block to other work on the current stream while the
+    kernels enqueued on `stream` still use it."""
+    if stream is None:
+        return new_workspace(nbytes, device)
+    with torch.cuda.stream(stream):
+        return new_workspace(nbytes, device)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -167,8 +222,9 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
     _need(tuple(v_cache.shape) == (NB, KVH, D, BLOCK_SIZE), "v_cache must be [NB, KVH, D, 16]")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T, "slot_mapping: int64 [T]")
     for t in (k, v, k_cache, v_cache):
-        _need(t.dtype == k.dtype and t.is_contiguous() and t.is_cuda, "same dtype, contiguous, on the GPU")
-    _need(slot_mapping.is_contiguous() and slot_mapping.is_cuda, "slot_mapping must be a contiguous GPU tensor")
+        _need(t.dtype == k.dtype and t.is_contiguous(), "same dtype, contiguous")
+    _need(slot_mapping.is_contiguous(), "slot_mapping must be contiguous")
+    _on_gpu_like(k, "kv_cache_write", v, k_cache, v_cache, slot_mapping)
     rc = lib.pkv_kv_cache_write(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
                                 T, NB, KVH, D, BLOCK_SIZE, _dtype_code(k), _stream(stream))
     _check(rc, "pkv_kv_cache_write")
@@ -187,7 +243,8 @@ def kv_cache_write_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Ten
           "k_cache [NB, KVH, 16, D], v_cache [NB, KVH, D, 16]")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T, "slot_mapping: int64 [T]")
     for t in (k, v, k_cache, v_cache, slot_mapping):
-        _need(t.is_contiguous() and t.is_cuda, "contiguous, on the GPU")
+        _need(t.is_contiguous(), "contiguous")
+    _on_gpu_like(k, "kv_cache_write_fp8", v, k_cache, v_cache, slot_mapping)
     rc = lib.pkv_kv_cache_write_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), T, NB, KVH,
                                     D, BLOCK_SIZE, float(k_scale), float(v_scale), _stream(stream))
     _check(rc, "pkv_kv_cache_write_fp8")
@@ -217,21 +274,6 @@ def decode_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv
     return {k: getattr(info, k) for k, _ in DecodePlanInfo._fields_}
 
 
-def probe_page_stream(k_cache: torch.Tensor, v_cache: torch.Tensor, page_index: torch.Tensor,
-                      wave_offsets: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """Measurement helper (include/pkv_probe.h): stream the listed K/V pages with the decode kernel's
-    load shapes and no arithmetic.  page_index / wave_offsets: int32 on the GPU."""
-    lib = load()
-    nb, kvh, B, D = k_cache.shape
-    _need(page_index.dtype == torch.int32 and wave_offsets.dtype == torch.int32, "int32 lists")
-    _need(k_cache.dtype in (torch.bfloat16, torch.uint8) and v_cache.dtype == k_cache.dtype
-          and v_cache.numel() == k_cache.numel() and B == BLOCK_SIZE, "bf16 or uint8 (E4M3) pools of one shape")
-    rc = lib.pkv_probe_page_stream(_ptr(k_cache), _ptr(v_cache), nb * kvh, D, k_cache.element_size(),
-                                   _ptr(page_index), _ptr(wave_offsets), wave_offsets.numel() - 1, _ptr(sink),
-                                   _stream(stream))
-    _check(rc, "pkv_probe_page_stream")
-
-
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       block_tables: torch.Tensor, context_lens: torch.Tensor,
                       q_lens: Optional[torch.Tensor], out: torch.Tensor, lse: Optional[torch.Tensor],
@@ -252,28 +294,14 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     not given.  `events` = (begin, end) torch.cuda.Event pair that has been recorded once: the library
     records them around its partition kernel."""
     lib = load()
-    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
-    total_q = q.shape[0]
-    S = context_lens.numel()
-    NB = k_cache.shape[0]
-    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
-    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
-    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    code = _decode_code(q, k_cache, v_cache, out)
-    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
-          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
-    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
-    if q_lens is not None:
-        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
-    if lse is not None:
-        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
-              "lse: fp32 [total_q, H]")
+    total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                                              num_heads, num_kv_heads, head_dim, block_size)
     o = _opts(partition_size, path, events, depth, schedule, wgs_per_cu, k_scale, v_scale)
     need = int(lib.pkv_decode_workspace_bytes(S, total_q, max_q_len, max_context_len, num_heads,
                                               num_kv_heads, head_dim, code, ctypes.byref(o)))
     if workspace is None and need > 0:
-        workspace = new_workspace(need, q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = _workspace_for(need, q.device, stream)
+    ws_bytes = _check_workspace(workspace, q)
     if new_k is None:
         rc = lib.pkv_paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                        _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),
@@ -285,7 +313,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _need(new_v is not None and new_k.shape == new_v.shape
           and tuple(new_k.shape) == (total_q, num_kv_heads, head_dim), "new_k / new_v must be [total_q, KVH, D]")
     for t in (new_k, new_v):
-        _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, contiguous, GPU")
+        _need(t.dtype == q.dtype and t.is_contiguous(), "new_k / new_v: q's dtype, contiguous")
+    _on_gpu_like(q, "new_k / new_v", new_k, new_v)
     rc = lib.pkv_paged_attn_decode_append(_ptr(q), _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache),
                                           _ptr(block_tables), _ptr(context_lens), _ptr(q_lens), _ptr(out),
                                           _ptr(lse), S, block_tables.shape[1], total_q, max_q_len,
@@ -307,26 +336,13 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_l
     on the GPU describe the groups; max_group_size / max_prefix_len are host-known bounds.  Other
     arguments as paged_attn_decode (bf16 q/out over bf16 or E4M3 pools)."""
     lib = load()
-    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
-    total_q = q.shape[0]
-    S = context_lens.numel()
-    NB = k_cache.shape[0]
-    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
-    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
-    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    code = _decode_code(q, k_cache, v_cache, out)
-    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
-          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
-    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
-    if q_lens is not None:
-        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
-    if lse is not None:
-        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
-              "lse: fp32 [total_q, H]")
+    total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                                              num_heads, num_kv_heads, head_dim, block_size)
     G = 0 if group_starts is None else group_starts.numel() - 1
     if G > 0:
         for t in (group_starts, prefix_lens, prefix_blocks):
-            _need(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda, "group arrays: int32, contiguous, GPU")
+            _need(t.dtype == torch.int32 and t.is_contiguous(), "group arrays: int32, contiguous")
+        _on_gpu_like(q, "group arrays", group_starts, prefix_lens, prefix_blocks)
         _need(prefix_lens.numel() == G and tuple(prefix_blocks.shape) == (G, max_prefix_len // block_size),
               "prefix_lens [G], prefix_blocks [G, max_prefix_len / 16]")
     o = _opts(partition_size, PATH_AUTO, events, depth, schedule, wgs_per_cu, k_scale, v_scale)
@@ -335,8 +351,8 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_l
                                                              num_kv_heads, head_dim, code, max(G, 0),
                                                              max_group_size, max_prefix_len, ctypes.byref(o)))
     if workspace is None:
-        workspace = new_workspace(need, q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+        workspace = _workspace_for(need, q.device, stream)
+    ws_bytes = _check_workspace(workspace, q)
     rc = lib.pkv_paged_attn_decode_shared_prefix(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(q_lens), _ptr(out),
         _ptr(lse), S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB, num_heads, num_kv_heads,
@@ -353,22 +369,8 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, q_lens, 
     [total_q, H, D] over bf16 pools or uint8 E4M3 pools (with their scales); the new tokens' K/V
     already written to the cache."""
     lib = load()
-    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
-    total_q = q.shape[0]
-    S = context_lens.numel()
-    NB = k_cache.shape[0]
-    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
-    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
-    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    code = _decode_code(q, k_cache, v_cache, out)
-    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
-          and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
-    _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
-    if q_lens is not None:
-        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
-    if lse is not None:
-        _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads) and lse.is_contiguous(),
-              "lse: fp32 [total_q, H]")
+    total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                                              num_heads, num_kv_heads, head_dim, block_size)
     o = _opts(0, PATH_AUTO, None, k_scale=k_scale, v_scale=v_scale)
     rc = lib.pkv_paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                                     _ptr(q_lens), _ptr(out), _ptr(lse), S, block_tables.shape[1], total_q, max_q_len,
@@ -401,24 +403,9 @@ class DecodeStep:
                  new_k=None, new_v=None, slot_mapping=None, wgs_per_cu=0, k_scale=0.0, v_scale=0.0):
         lib = load()
         self._lib = lib
-        total_q = q.shape[0]
-        S = context_lens.numel()
-        NB = k_cache.shape[0]
         # the full checks of the one-shot calls, once
-        _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [total_q, H, D]")
-        _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim), "k_cache [NB, KVH, 16, D]")
-        _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size), "v_cache [NB, KVH, D, 16]")
-        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-        code = _decode_code(q, k_cache, v_cache, out)
-        _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S
-              and block_tables.is_contiguous(), "block_tables: int32 [S, max_blocks], contiguous")
-        _need(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens: int32 [S]")
-        if q_lens is not None:
-            _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(),
-                  "q_lens: int32 [S]")
-        if lse is not None:
-            _need(lse.dtype == torch.float32 and tuple(lse.shape) == (total_q, num_heads)
-                  and lse.is_contiguous(), "lse: fp32 [total_q, H]")
+        total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out,
+                                                  lse, num_heads, num_kv_heads, head_dim, block_size)
         self._opts = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu, k_scale, v_scale)
         self._opts_ev = DecodeOptions(partition_size, path, depth, schedule, None, None, wgs_per_cu, k_scale,
                                       v_scale)
@@ -426,7 +413,7 @@ class DecodeStep:
                                                   num_kv_heads, head_dim, code, ctypes.byref(self._opts)))
         if workspace is None and need > 0:
             workspace = new_workspace(need, q.device)
-        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        ws_bytes = _check_workspace(workspace, q)
         _need(ws_bytes >= need, "workspace too small")
         self._keep = (q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse, workspace,
                       new_k, new_v, slot_mapping)
@@ -442,16 +429,18 @@ class DecodeStep:
                   and tuple(new_k.shape) == (total_q, num_kv_heads, head_dim),
                   "new_k / new_v must be [total_q, KVH, D] for the fused append")
             for t in (new_k, new_v):
-                _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, on the GPU")
+                _need(t.dtype == q.dtype and t.is_contiguous(), "new_k / new_v: q's dtype, contiguous")
+            _on_gpu_like(q, "new_k / new_v", new_k, new_v)
             self._fused = (_ptr(new_k), _ptr(new_v))
         if slot_mapping is not None:
             T = new_k.shape[0]
             _need(new_k.dim() == 3 and new_k.shape == new_v.shape and tuple(new_k.shape[1:]) == (num_kv_heads, head_dim),
                   "new_k / new_v must be [T, KVH, D]")
-            _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T and slot_mapping.is_contiguous()
-                  and slot_mapping.is_cuda, "slot_mapping: int64 [T] on the GPU")
+            _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T and slot_mapping.is_contiguous(),
+                  "slot_mapping: int64 [T], contiguous")
             for t in (new_k, new_v):
-                _need(t.dtype == q.dtype and t.is_contiguous() and t.is_cuda, "new_k / new_v: q's dtype, on the GPU")
+                _need(t.dtype == q.dtype and t.is_contiguous(), "new_k / new_v: q's dtype, contiguous")
+            _on_gpu_like(q, "appended rows", new_k, new_v, slot_mapping)
             if code == PKV_BF16_FP8KV:
                 _need(k_scale > 0 and v_scale > 0, "E4M3 pools need k_scale / v_scale > 0 for the write")
                 self._write = ((_ptr(new_k), _ptr(new_v), _ptr(slot_mapping)),

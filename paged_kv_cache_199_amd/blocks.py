@@ -12,7 +12,7 @@ from typing import List, Optional, Sequence as Seq, Tuple
 import numpy as np
 import torch
 
-from ._lib import BLOCK_SIZE, _check, _need, _ptr, _stream, load
+from ._lib import BLOCK_SIZE, _check, _need, _on_gpu_like, _ptr, _stream, load
 
 ERR_WORKSPACE = -4   # pkv_status: the pool has too few free blocks
 
@@ -181,7 +181,8 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,
         k_cache.shape[0], k_cache.shape[1], k_cache.shape[3], BLOCK_SIZE) and v_cache.dtype == k_cache.dtype,
         "k_cache [NB, KVH, 16, D], v_cache [NB, KVH, D, 16], one dtype")
     for t in (k_cache, v_cache, src, dst):
-        _need(t.is_contiguous() and t.is_cuda, "contiguous, on the GPU")
+        _need(t.is_contiguous(), "contiguous")
+    _on_gpu_like(k_cache, "copy_blocks", v_cache, src, dst)
     NB, KVH, _, D = k_cache.shape
     rc = lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src), _ptr(dst), src.numel(), NB, KVH, D,
                              k_cache.element_size(), _stream(stream))

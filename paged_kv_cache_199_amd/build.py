@@ -16,8 +16,10 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
-           "decode_combine.hip", "stream_probe.hip", "block_manager.hip",
-           "decode_prefix.hip", "prefill_mfma.hip"]
+           "decode_combine.hip", "block_manager.hip", "decode_prefix.hip", "prefill_mfma.hip"]
+# the benchmark's page-stream probe (include/pkv_probe.h) is a library of its own, not part of libpkv.so
+PROBE_SOURCES = ["stream_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -56,14 +58,16 @@ def _finish(p, verbose):
 
 
 def build_library(verbose: bool = False) -> str:
-    """Every source to an object (in parallel), then one shared library."""
+    """Every source to an object (in parallel), then the shared libraries: libpkv.so (the product) and
+    libpkv_probe.so (the benchmark's page-stream probe)."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
-    objs, pending = [], []
-    for src in SOURCES:
+    all_src = SOURCES + PROBE_SOURCES
+    jobs = max(1, min(len(all_src), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    objs, pending = {}, []
+    for src in all_src:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        objs.append(obj)
+        objs[src] = obj
         extra = [] if src in AGPR_ACC else VGPR_FORM
         pending.append([hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     running = []
@@ -71,10 +75,11 @@ def build_library(verbose: bool = False) -> str:
         while pending and len(running) < jobs:
             running.append(_run(pending.pop(0), verbose))
         _finish(running.pop(0), verbose)
-    tmp = LIB + ".tmp"
-    p = _run([hipcc(), "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    _finish(p, verbose)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        p = _run([hipcc(), "-shared", f"--offload-arch={ARCH}", *[objs[x] for x in srcs], "-o", tmp], verbose)
+        _finish(p, verbose)
+        os.replace(tmp, lib)
     return LIB
 
 
