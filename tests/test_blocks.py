@@ -279,3 +279,105 @@ def test_random_operations_follow_the_model(seed):
     counts = _random_run(seed)
     # the run exercised the interesting paths
     assert min(counts.values()) > 0
+
+
+# ---- the reference model's prefix cache on its own, pinned by hand-worked cases ----
+# Each expected value below is worked out by hand from the rules in oracle/block_manager.py's header:
+# only whole 16-token blocks are cached, a match is the longest cached run of whole blocks from the
+# start, and eviction takes the least recently used entry that has no cached extension (a leaf) and
+# no holder but the cache.
+
+
+def _model_prefix_case(M):
+    """Longest match, whole blocks only, re-insert keeps the cached blocks, held blocks stay."""
+    m = M(10)
+    toks = [t % 7 for t in range(40)]
+    m.new_seq(0)
+    m.append(0, 40, [3, 5, 7])
+    assert m.insert(toks, [3, 5, 7]) == 2                     # 40 tokens = 2 whole blocks + 8 tokens
+    assert sorted(len(k) for k in m.cache) == [16, 32]        # the 8-token tail is not cached
+    assert m.refcount(3) == 2 and m.refcount(5) == 2 and m.refcount(7) == 1
+    assert m.match(toks[:35]) == [3, 5]
+    assert m.match(toks[:20] + [99] * 20) == [3]              # the second block differs after 4 tokens
+    assert m.match(toks[:15]) == []                           # less than one whole block
+    assert m.match([t + 1 for t in toks]) == []
+    assert m.insert(toks + [1] * 8, [8, 9, 4]) == 1           # third block new; the first two keep 3, 5
+    assert m.match(toks + [1] * 8) == [3, 5, 4]
+    assert m.evict(9) == 1                                    # only the new leaf: 3 and 5 are held
+    assert m.match(toks + [1] * 8) == [3, 5]
+    m.drop_seq(0)
+    assert m.refcount(3) == 1 and m.refcount(7) == 0
+    assert m.evict(1) == 1 and m.match(toks) == [3]           # the leaf toks[:32] goes before its parent
+    assert m.evict(4) == 1 and not m.cache
+
+
+def _model_lru_case(M):
+    """Least recently used leaf first; a match counts as a use; a held leaf is passed over."""
+    m = M(8)
+    x, y, z = [0] * 32, [1] * 16, [2] * 16
+    assert m.insert(x, [0, 1]) == 2 and m.insert(y, [2]) == 1 and m.insert(z, [3]) == 1
+    assert m.match(x) == [0, 1]                               # x is now more recent than y and z
+    m.new_seq(0)
+    m.adopt(0, [2])                                           # y's block gets a holder
+    assert m.evict(1) == 1                                    # y is the oldest leaf but held: z goes
+    assert m.match(z) == [] and m.match(y) == [2]             # (and y is now the most recent)
+    m.drop_seq(0)
+    assert m.evict(1) == 1 and m.match(x) == [0]              # leaves x[:32] (older) and y: x[:32] goes
+    assert m.evict(1) == 1 and m.match(y) == []               # leaves x[:16] (just used) and y: y goes
+    assert m.evict(3) == 1 and not m.cache
+
+
+def test_block_model_prefix_cache_by_hand():
+    _model_prefix_case(BlockModel)
+    _model_lru_case(BlockModel)
+
+
+class _CachesPartialBlocks(BlockModel):
+    def insert(self, tokens, blocks):
+        return super().insert(list(tokens) + [0] * (-len(tokens) % BLOCK), list(blocks) + [0, 0])
+
+
+class _MatchDoesNotTouch(BlockModel):
+    def match(self, tokens):
+        saved = dict(self.cache)
+        out = super().match(tokens)
+        self.cache = saved
+        return out
+
+
+class _EvictsHeldBlocks(BlockModel):
+    def evict(self, n):
+        freed = 0
+        while freed < n:
+            cands = [(used, key) for key, (blk, used) in self.cache.items() if not self._has_extension(key)]
+            if not cands:
+                break
+            del self.cache[min(cands)[1]]
+            freed += 1
+        return freed
+
+
+class _EvictsInnerNodes(BlockModel):
+    def _has_extension(self, key):
+        return False
+
+
+class _MostRecentFirst(BlockModel):
+    def evict(self, n):
+        freed = 0
+        while freed < n:
+            cands = [(used, key) for key, (blk, used) in self.cache.items()
+                     if not self._has_extension(key) and self.refcount(blk) == 1]
+            if not cands:
+                break
+            del self.cache[max(cands)[1]]
+            freed += 1
+        return freed
+
+
+@pytest.mark.parametrize("mutant", [_CachesPartialBlocks, _MatchDoesNotTouch, _EvictsHeldBlocks, _EvictsInnerNodes,
+                                    _MostRecentFirst])
+def test_planted_prefix_cache_mistakes_fail_a_hand_case(mutant):
+    with pytest.raises(AssertionError):
+        _model_prefix_case(mutant)
+        _model_lru_case(mutant)

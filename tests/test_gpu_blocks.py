@@ -9,7 +9,7 @@ from oracle import paged_attention as O
 from oracle.block_manager import copy_blocks as model_copy
 from paged_kv_cache_199_amd import _lib
 from paged_kv_cache_199_amd.blocks import BlockPool, RadixIndex, Sequence, copy_blocks
-from tests.gpu_helpers import BF16_TOL, LSE_TOL, host_bits
+from tests.gpu_helpers import (BF16_TOL, LSE_TOL, host_bits, nan_empty)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -91,8 +91,8 @@ def test_prefix_sharing_and_copy_on_write_decode(gpu_lib):
         t = s.block_table()
         bt[i, :len(t)] = t
     q = torch.from_numpy(rng.standard_normal((3, H, D))).to(torch.bfloat16)
-    out = torch.empty((3, H, D), dtype=torch.bfloat16, device=DEV)
-    lse = torch.empty((3, H), dtype=torch.float32, device=DEV)
+    out = nan_empty((3, H, D), DEV, torch.bfloat16)
+    lse = nan_empty((3, H), DEV)
     scale = 1.0 / np.sqrt(D)
     _lib.paged_attn_decode(q.to(DEV), kc, vc, torch.from_numpy(bt).to(DEV),
                            torch.tensor(lens, dtype=torch.int32, device=DEV), None, out, lse, H, KVH, D, 16,

@@ -11,7 +11,7 @@ import torch
 from oracle import paged_attention as O
 from paged_kv_cache_199_amd import _lib
 from paged_kv_cache_199_amd import workloads as W
-from tests.gpu_helpers import BF16_TOL, LSE_TOL, compare, host_bits, oracle_full
+from tests.gpu_helpers import (BF16_TOL, LSE_TOL, compare, host_bits, nan_empty, nan_like, oracle_full)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -39,8 +39,8 @@ def _small_append_workload():
 def test_bound_step_matches_one_shot_calls_and_oracle(gpu_lib):
     w = _small_append_workload()
     kc0, vc0 = host_bits(w.k_cache), host_bits(w.v_cache)
-    out = torch.empty_like(w.q)
-    lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=DEV)
+    out = nan_like(w.q)
+    lse = nan_empty((w.total_q, w.spec.num_heads), DEV)
     _step_for(w, out, lse)()
     torch.cuda.synchronize()
     # the append is in the cache, bit for bit
@@ -52,8 +52,8 @@ def test_bound_step_matches_one_shot_calls_and_oracle(gpu_lib):
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
     # the one-shot entry point on the same (already appended) cache gives the same bits
     meta = w.device_meta(DEV)
-    out2 = torch.empty_like(out)
-    lse2 = torch.empty_like(lse)
+    out2 = nan_like(out)
+    lse2 = nan_like(lse)
     _lib.paged_attn_decode(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"], None, out2,
                            lse2, w.spec.num_heads, w.spec.num_kv_heads, w.spec.head_dim, 16, w.scale,
                            w.max_context_len, max_q_len=w.max_q_len)
@@ -64,8 +64,8 @@ def test_bound_step_matches_one_shot_calls_and_oracle(gpu_lib):
 @pytest.mark.parametrize("schedule", [_lib.SCHEDULE_PERSISTENT, _lib.SCHEDULE_GRID])
 def test_graph_replays_match_eager(gpu_lib, schedule):
     w = _small_append_workload()
-    out = torch.empty_like(w.q)
-    lse = torch.empty((w.total_q, w.spec.num_heads), dtype=torch.float32, device=DEV)
+    out = nan_like(w.q)
+    lse = nan_empty((w.total_q, w.spec.num_heads), DEV)
     step = _step_for(w, out, lse, schedule=schedule)
     step()
     torch.cuda.synchronize()
@@ -91,7 +91,7 @@ def test_graph_replays_match_eager(gpu_lib, schedule):
         assert torch.equal(_bits(out), _bits(want_out)) and torch.equal(lse, want_lse)
         assert torch.equal(_bits(w.k_cache), _bits(want_k)) and torch.equal(_bits(w.v_cache), _bits(want_v))
         # eager work of the program between replays
-        o2 = torch.empty_like(other.q)
+        o2 = nan_like(other.q)
         m2 = other.device_meta(DEV)
         _lib.paged_attn_decode(other.q, other.k_cache, other.v_cache, m2["block_tables"], m2["context_lens"],
                                None, o2, None, 8, 2, 128, 16, other.scale, other.max_context_len)
