@@ -138,6 +138,10 @@ int pkv_kv_cache_write_fp8(const void *k, const void *v, const int64_t *slot_map
                            float k_scale, float v_scale, void *stream);
 
 /*
+ * Workspace query.  The lfm25-inference page ("Runtime Design") runs its decode without allocating per
+ * step, with temporary device memory taken from bounded, reused pools; here the caller owns that
+ * memory and this call says how much one decode call needs, so a serving loop sizes it once and
+ * reuses it for every step.
  * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options (0 is possible:
  * a single-partition grid launch with uniform q needs none).  The split-K partials take
  * ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes; the persistent
@@ -216,7 +220,9 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
                                  float scale, int dtype, const pkv_decode_options *opts,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Human-readable text for a pkv_status value (static storage). */
+/* Human-readable text for a pkv_status value (static storage): the error side of the boundary, which,
+ * like the lfm25-inference page's runtime ("Runtime Design": an engine that owns its pages and
+ * memory), reports a refused call to its caller instead of allocating or failing on the device. */
 const char *pkv_status_string(int status);
 
 /* ABI version of this header: (major << 16) | minor. */
