@@ -2,14 +2,18 @@
 sequence's new K/V row (when the workload has one) plus paged decode attention with its split-K
 combine, all through the C ABI.
 
-    python bench.py [--steps K] [--warmup W] [--workload conc32_bf16] [--partition-size P]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition-size P]
 
-Prints ONE JSON line.  `value` is whole-step throughput in GB/s of algorithmic bytes (every attended
-K/V row once, Q, the output, the LSE, the block ids and lengths, plus the appended rows), with every
-input resident in HBM before the clock starts.  The K/V pool is cloned into enough copies (>= 1 GiB in
-total) that consecutive steps never hit the 256 MB Infinity Cache; step i uses copy i mod R.
-`roofline` reports the partition kernel alone, timed by HIP events the library records around it on
-the launch stream.  `cpu_baseline` times the float64 oracle on the host on a bounded sample.
+Prints ONE JSON line.  With no --workload it is the long-context configuration (256 sequences,
+lognormal contexts up to 32768 tokens, 64 query / 8 kv heads): the largest that fits one GPU.  Its
+fixed 512-key-partition variant rides along under "variants", and the concurrency-32 step (with its
+slot_mapping-write variant) under "secondary".  `value` is whole-step throughput in GB/s of algorithmic
+bytes (every attended K/V row once, Q, the output, the LSE, the block ids and lengths, plus the
+appended rows), with every input resident in HBM before the clock starts.  The K/V pool is cloned into
+enough copies (>= 1 GiB in total) that consecutive steps never hit the 256 MB Infinity Cache; step i
+uses copy i mod R.  `roofline` reports the partition kernel alone, timed by HIP events the library
+records around it on the launch stream.  `cpu_baseline` times the float64 oracle on every host core
+on a bounded sample.
 """
 from __future__ import annotations
 
@@ -214,56 +218,134 @@ def pattern_ceiling(w, plan, kcs, vcs, reps: int = 3):
     return a.elapsed_time(b) * 1e-3 / n, int(offs[-1])
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle as it is, single-threaded BLAS, on whole sequences (cycling through the workload)
-    until ~budget_s of CPU work."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Host bytes of K/V pages the CPU baseline copies out for its sample of sequences (it cycles over them).
+CPU_SAMPLE_BYTES = 1 << 30
+
+
+def _oracle_worker(job):
+    """One host core's share of the CPU baseline (runs in a spawned process): the oracle, unchanged, on
+    whole sequences of the sample (cycling from this worker's offset) until the shared deadline, with
+    one BLAS thread.  Returns (units, tokens, calls): units are bytes ("bytes") or matrix flops
+    ("flops") by the GPU figure's own numerator."""
+    root, files, p, start, deadline = job
+    if root not in sys.path:
+        sys.path.insert(0, root)
     from threadpoolctl import threadpool_limits
 
+    from oracle import fp8 as F8
     from oracle import paged_attention as O
+
+    a = {k: np.load(f, mmap_mode="r") for k, f in files.items()}
+    q, kc, vc, table, ctx, ql = a["q"], a["kc"], a["vc"], a["table"], a["ctx"], a["ql"]
+    S, B, KVH, H, D = len(ctx), p["block"], p["kvh"], p["heads"], p["dim"]
+    units = tokens = calls = 0
+    i = start
+    with threadpool_limits(limits=1):
+        while time.time() < deadline:
+            s = i % S
+            i += 1
+            n, qs = int(ctx[s]), int(ql[s])
+            if p["fp8"]:
+                ids = np.asarray(table[s, :(n + B - 1) // B], dtype=np.int64)
+                kd, vd = F8.dequantize(kc[ids], p["k_scale"]), F8.dequantize(vc[ids], p["v_scale"])
+                t1 = np.full_like(np.asarray(table), -1)
+                t1[s, :ids.shape[0]] = np.arange(ids.shape[0])
+                O.paged_decode_attention(q, kd, vd, t1, ctx, ql, p["scale"], KVH, B, seqs=[s])
+            else:
+                O.paged_decode_attention(q, kc, vc, table, ctx, ql, p["scale"], KVH, B, seqs=[s])
+            if p["count"] == "flops":
+                units += (qs * (n - qs) + qs * (qs + 1) // 2) * H * 4 * D
+            else:
+                units += n * KVH * D * 2 * p["ekv"] + qs * H * (D * p["e"] * 2 + 4) + ((n + B - 1) // B) * 4 + 8
+            tokens += n
+            calls += 1
+    return units, tokens, calls
+
+
+def oracle_on_all_cores(w, budget_s: float, count: str = "bytes"):
+    """The oracle on every core this process may use (os.sched_getaffinity), one spawned worker process
+    per core with one BLAS thread each (so BLAS runs as many threads as there are cores), for about
+    budget_s of wall time.  The sample: the workload's first sequences whose pages fit CPU_SAMPLE_BYTES
+    (all of them when they fit), copied to memory-mapped files the workers share, with the block tables
+    renumbered to the copied pages.  Returns (units, tokens, calls, cores, wall seconds, sequences)."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
     import torch
 
     def bits(t):
         t = t.detach().cpu().contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    from oracle import fp8 as F8
-
-    q, kc, vc = bits(w.q), bits(w.k_cache), bits(w.v_cache)
     B = w.spec.block_size
-    e = 4 if w.spec.dtype == "f32" else 2
-    ekv = 1 if w.kv_fp8 else e
-    t_used, nbytes, tokens, n_runs = 0.0, 0, 0, 0
-    with threadpool_limits(limits=1):
-        while t_used < budget_s:
-            s = n_runs % w.num_seqs
-            n = int(w.context_lens[s])
-            t0 = time.perf_counter()
-            if w.kv_fp8:
-                # E4M3 pools: decode the sequence's pages (part of the oracle's work), then attend
-                ids = w.block_tables[s, :(n + B - 1) // B].astype(np.int64)
-                kd = F8.dequantize(kc[ids], w.spec.k_scale)
-                vd = F8.dequantize(vc[ids], w.spec.v_scale)
-                table = np.full_like(w.block_tables, -1)
-                table[s, :ids.shape[0]] = np.arange(ids.shape[0])
-                O.paged_decode_attention(q, kd, vd, table, w.context_lens, w.q_lens, w.scale, w.spec.num_kv_heads,
-                                         B, seqs=[s])
-            else:
-                O.paged_decode_attention(q, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale,
-                                         w.spec.num_kv_heads, B, seqs=[s])
-            t_used += time.perf_counter() - t0
-            qs = int(w.q_lens[s])
-            nbytes += n * w.spec.num_kv_heads * w.spec.head_dim * 2 * ekv + qs * w.spec.num_heads * (
-                w.spec.head_dim * e * 2 + 4) + ((n + B - 1) // B) * 4 + 8
-            tokens += n
-            n_runs += 1
+    nblk = (w.context_lens.astype(np.int64) + B - 1) // B
+    page_bytes = w.spec.num_kv_heads * B * w.spec.head_dim * 2 * w.k_cache.element_size()
+    n_seq = int(max(1, min(w.num_seqs, np.searchsorted(np.cumsum(nblk) * page_bytes, CPU_SAMPLE_BYTES,
+                                                          side="right"))))
+    ids = np.concatenate([w.block_tables[s, :nblk[s]] for s in range(n_seq)]).astype(np.int64)
+    uniq = np.unique(ids)
+    remap = np.full(w.num_blocks, -1, np.int32)
+    remap[uniq] = np.arange(uniq.shape[0], dtype=np.int32)
+    table = np.where(w.block_tables[:n_seq] >= 0, remap[np.maximum(w.block_tables[:n_seq], 0)], -1).astype(np.int32)
+    sel = torch.from_numpy(uniq).to(w.k_cache.device)
+    q_rows = int(w.q_lens[:n_seq].sum())
+    arrays = {"q": bits(w.q[:q_rows]), "kc": bits(w.k_cache.index_select(0, sel)),
+              "vc": bits(w.v_cache.index_select(0, sel)), "table": table,
+              "ctx": w.context_lens[:n_seq].copy(), "ql": w.q_lens[:n_seq].copy()}
+    need = sum(x.nbytes for x in arrays.values())
+    base = "/dev/shm" if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > 2 * need else None
+    tmp = tempfile.mkdtemp(prefix="pkv_cpu_", dir=base)
+    try:
+        files = {}
+        for k, x in arrays.items():
+            files[k] = os.path.join(tmp, k + ".npy")
+            np.save(files[k], x)
+        del arrays
+        e = 4 if w.spec.dtype == "f32" else 2
+        p = {"block": B, "kvh": w.spec.num_kv_heads, "heads": w.spec.num_heads, "dim": w.spec.head_dim,
+             "scale": w.scale, "fp8": w.kv_fp8, "k_scale": w.spec.k_scale, "v_scale": w.spec.v_scale,
+             "e": e, "ekv": 1 if w.kv_fp8 else e, "count": count}
+        cores = len(os.sched_getaffinity(0))
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores) as pool:
+            # start every worker and load its imports before the clock starts
+            pool.map(_oracle_worker, [(ROOT, files, p, 0, 0.0)] * cores, chunksize=1)
+            t0 = time.time()
+            jobs = [(ROOT, files, p, k * n_seq // cores, t0 + budget_s) for k in range(cores)]
+            parts = pool.map(_oracle_worker, jobs, chunksize=1)
+            wall = time.time() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return (sum(x[0] for x in parts), sum(x[1] for x in parts), sum(x[2] for x in parts), cores, wall, n_seq)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it is, on whole sequences of the workload (cycling over a sample of them), on every
+    core of the host, for about budget_s of wall time.  Same numerator as the GPU figure: each
+    sequence's K/V bytes, its q/out/lse rows, page ids and lengths."""
+    nbytes, tokens, calls, cores, wall, n_seq = oracle_on_all_cores(w, budget_s)
     return {
-        "value": round(nbytes / t_used / 1e9, 4),
+        "value": round(nbytes / wall / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": f"{n_runs} sequence decodes cycling over the {w.num_seqs} sequences of the workload "
-                  f"({tokens} context tokens, all heads), numpy float64, 1 BLAS thread, {t_used:.1f} s",
-        "attended_tokens_per_s": round(tokens / t_used, 1),
+        "sample": f"{calls} sequence decodes cycling over the first {n_seq} of the workload's {w.num_seqs} "
+                  f"sequences ({tokens} context tokens, all heads), numpy float64, {cores} worker processes "
+                  f"with one BLAS thread each, {wall:.1f} s wall",
+        "attended_tokens_per_s": round(tokens / wall, 1),
     }
 
 
@@ -341,7 +423,7 @@ def bench_blocks(args, dev):
             done += 1
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(done / dt, 1), "unit": "slot allocations/s", "cores": 1,
-                               "kind": "oracle",
+                               "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"{done} one-token appends on 64 sequences of 1000+ tokens through the "
                                          f"oracle's reference model of the block manager, {dt:.1f} s"}
     print(json.dumps(res), flush=True)
@@ -429,101 +511,29 @@ def bench_prefill(args, dev, spec):
                      "kernel": "prefill_mfma_kernel", "kernel_ms": round(ms, 5), "flops_per_launch": flops},
     }
     if args.cpu_budget > 0:
-        from threadpoolctl import threadpool_limits
-
-        from oracle import paged_attention as O
-
-        def bits(t):
-            t = t.detach().cpu().contiguous()
-            return t.view(torch.int16).numpy().view(np.uint16)
-
-        qh = bits(w.q)
-        if spec.kv_fp8:
-            from oracle import fp8 as F8
-
-            kc = F8.dequantize(w.k_cache.cpu().numpy(), spec.k_scale)
-            vc = F8.dequantize(w.v_cache.cpu().numpy(), spec.v_scale)
-        else:
-            kc, vc = bits(w.k_cache), bits(w.v_cache)
-        done, t_used, n = 0, 0.0, 0
-        with threadpool_limits(limits=1):
-            while t_used < min(args.cpu_budget, 20.0):
-                s_ = n % w.num_seqs
-                t0 = time.perf_counter()
-                O.paged_decode_attention(qh, kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale, KVH,
-                                         spec.block_size, seqs=[s_])
-                t_used += time.perf_counter() - t0
-                c, qq = int(w.context_lens[s_]), int(w.q_lens[s_])
-                done += (qq * (c - qq) + qq * (qq + 1) // 2) * H * 4 * D
-                n += 1
-        res["cpu_baseline"] = {"value": round(done / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"{n} whole sequences of the workload (all heads), numpy float64, "
-                                         f"1 BLAS thread, {t_used:.1f} s"}
+        done, _, n, cores, wall, n_seq = oracle_on_all_cores(w, min(args.cpu_budget, 20.0), count="flops")
+        res["cpu_baseline"] = {"value": round(done / wall / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                               "cpu_model": cpu_model(), "kind": "oracle",
+                               "sample": f"{n} whole sequences cycling over the first {n_seq} of the workload "
+                                         f"(all heads), numpy float64, {cores} worker processes with one BLAS "
+                                         f"thread each, {wall:.1f} s wall"}
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="conc32_bf16")
-    ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own, 0: policy")
-    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--depth", type=int, default=0, help="MFMA register ring depth (0: policy)")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
-    ap.add_argument("--wgs-per-cu", type=int, default=0, help="persistent grid: workgroups per CU (0: policy)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
-    ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
-    ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
-    ap.add_argument("--no-graph", action="store_true", help="time the eager step only")
-    ap.add_argument("--append", default="fused", choices=["fused", "slots"],
-                    help="appending workloads: write the new tokens inside the decode call (fused) or "
-                         "with pkv_kv_cache_write through slot_mapping first (slots)")
-    ap.add_argument("--prefix-mode", default="auto", choices=["auto", "once", "per-seq", "off"],
-                    help="shared-prefix workloads: pkv_paged_attn_decode_shared_prefix with the library's "
-                         "policy (auto), forced read-once (once) or per-sequence (per-seq); off: plain "
-                         "pkv_paged_attn_decode")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy (for counter calibration)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure_decode(args, dev, spec, w=None, **override):
+    """One decode workload timed as the bench line describes (graph replay of K steps, HIP events around
+    the partition kernel, pattern ceiling).  `override` replaces command-line options for this run (e.g.
+    partition_size, append, no_ceiling).  The built workload comes back under "_workload"."""
     import torch
 
     from paged_kv_cache_199_amd import _lib
     from paged_kv_cache_199_amd import workloads as W
 
-    _lib.load()
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-
-    if args.calibrate_copy:
-        n = 1 << 28
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 5}))
-        return
-
-    if args.workload == "blocks_cow":
-        bench_blocks(args, dev)
-        return
-
-    spec = W.named(args.workload)
-    if spec.prefill:
-        bench_prefill(args, dev, spec)
-        return
+    args = argparse.Namespace(**{**vars(args), **override})
     P = spec.partition_size if args.partition_size < 0 else args.partition_size
     path = {"auto": _lib.PATH_AUTO, "valu": _lib.PATH_VALU, "mfma": _lib.PATH_MFMA}[args.path]
-    w = W.build(spec, dev)
+    if w is None:
+        w = W.build(spec, dev)
     meta = w.device_meta(dev)
     H, KVH, D = spec.num_heads, spec.num_kv_heads, spec.head_dim
     pool_bytes = w.k_cache.numel() * w.k_cache.element_size() * 2
@@ -719,8 +729,129 @@ def main():
                     "and no arithmetic",
         }
         res["roofline"]["frac_of_pattern_ceiling"] = round(achieved / ceil, 4)
+    res["_workload"] = w
+    return res
+
+
+# The default line: the largest configuration that fits one GPU (256 sequences, 64 query / 8 kv heads,
+# lognormal contexts up to 32768 tokens), with the concurrency-32 step nested beside it.
+DEFAULT_WORKLOAD = "long_ctx_splitk_bf16"
+SECONDARY_WORKLOAD = "conc32_bf16"
+
+
+def _summary(r):
+    """The figures of one measured run that a variant or nested line carries."""
+    ro = r["roofline"]
+    out = {"ms_per_step": r["ms_per_step"], "value": r["value"], "unit": r["unit"],
+           "frac_of_hbm_peak": r["frac_of_hbm_peak"], "attended_tokens_per_s": r["attended_tokens_per_s"],
+           "algorithmic_bytes_per_step": r["algorithmic_bytes_per_step"],
+           "partition_size": r["config"]["partition_size"], "append": r["config"]["append"],
+           "eager_ms_per_step": r["eager_ms_per_step"],
+           "roofline": {k: ro[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                           "kernel_ms", "algorithmic_bytes_per_launch")}}
+    for k in ("pattern_ceiling", "frac_of_pattern_ceiling"):
+        if k in ro:
+            out["roofline"][k] = ro[k]
+    return out
+
+
+def default_line(args, dev):
+    """The long-context step (library policy: the balanced split), its variant with fixed 512-key
+    partitions (the configuration's own wording), the oracle on the host's cores, and the
+    concurrency-32 step (fused append, and the slot_mapping write + decode variant) nested under
+    "secondary"."""
+    from paged_kv_cache_199_amd import workloads as W
+
+    res = measure_decode(args, dev, W.named(DEFAULT_WORKLOAD))
+    w = res.pop("_workload")
+    v512 = measure_decode(args, dev, w.spec, w=w, partition_size=512, no_ceiling=True)
+    v512.pop("_workload")
+    res["variants"] = {"partition_512": {
+        "what": "the same step with fixed 512-key partitions merged through their LSE; the default line lets "
+                "the balanced persistent schedule cut each sequence where its wave shares end",
+        **_summary(v512)}}
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    del w
+    conc = measure_decode(args, dev, W.named(SECONDARY_WORKLOAD))
+    cw = conc.pop("_workload")
+    slots = measure_decode(args, dev, cw.spec, w=cw, append="slots", no_ceiling=True)
+    slots.pop("_workload")
+    nested = {"workload": SECONDARY_WORKLOAD, "config": conc["config"], **_summary(conc)}
+    nested["variants"] = {"slot_mapping_write": {
+        "what": "pkv_kv_cache_write of the 32 new tokens through slot_mapping, then pkv_paged_attn_decode "
+                "(two calls); the nested line appends inside the decode call (bit-identical result)",
+        **_summary(slots)}}
+    res["secondary"] = {SECONDARY_WORKLOAD: nested}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help="one workload by name; default: the long-context line with conc32 nested")
+    ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own, 0: policy")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--depth", type=int, default=0, help="MFMA register ring depth (0: policy)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
+    ap.add_argument("--wgs-per-cu", type=int, default=0, help="persistent grid: workgroups per CU (0: policy)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work; 0 skips")
+    ap.add_argument("--min-pool-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the page-stream ceiling probe")
+    ap.add_argument("--no-graph", action="store_true", help="time the eager step only")
+    ap.add_argument("--append", default="fused", choices=["fused", "slots"],
+                    help="appending workloads: write the new tokens inside the decode call (fused) or "
+                         "with pkv_kv_cache_write through slot_mapping first (slots)")
+    ap.add_argument("--prefix-mode", default="auto", choices=["auto", "once", "per-seq", "off"],
+                    help="shared-prefix workloads: pkv_paged_attn_decode_shared_prefix with the library's "
+                         "policy (auto), forced read-once (once) or per-sequence (per-seq); off: plain "
+                         "pkv_paged_attn_decode")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_199_amd import _lib
+    from paged_kv_cache_199_amd import workloads as W
+
+    _lib.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = 1 << 28
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_each_way": n * 4, "launches": 5}))
+        return
+
+    if args.workload == "blocks_cow":
+        bench_blocks(args, dev)
+        return
+
+    if args.workload is None:
+        print(json.dumps(default_line(args, dev)), flush=True)
+        return
+    spec = W.named(args.workload)
+    if spec.prefill:
+        bench_prefill(args, dev, spec)
+        return
+    res = measure_decode(args, dev, spec)
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(res.pop("_workload"), args.cpu_budget)
+    res.pop("_workload", None)
     print(json.dumps(res), flush=True)
 
 

@@ -82,3 +82,16 @@ def test_probe_page_lists_cover_every_page_once():
                     assert len(lists) == waves
                     got = np.sort(np.concatenate(lists))
                     assert np.array_equal(got, np.sort(np.asarray(want, np.int64)))
+
+
+def test_cpu_baseline_uses_every_core_and_names_the_cpu():
+    """The oracle baseline runs one worker process per core of the affinity set and records the CPU
+    model; its bytes count the same numerator as the GPU figure."""
+    import os
+
+    import bench
+
+    w = W.build(W.custom("cpu_base", [17, 300, 64], num_heads=8, num_kv_heads=2, head_dim=64), "cpu")
+    r = bench.cpu_baseline(w, 0.5)
+    assert r["cores"] == len(os.sched_getaffinity(0)) and r["kind"] == "oracle"
+    assert r["cpu_model"] and r["value"] > 0 and "worker processes" in r["sample"]
