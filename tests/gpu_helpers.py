@@ -72,12 +72,30 @@ def _pools(w: Workload, kc, vc):
     return kc, vc
 
 
+def abs_values(pool: np.ndarray) -> np.ndarray:
+    """|x| of a host pool: bf16 bit patterns lose their sign bit, float arrays their sign (NaN stays NaN)."""
+    if pool.dtype == np.uint16:
+        return pool & np.uint16(0x7FFF)
+    return np.abs(pool)
+
+
+def oracle_with_vabs(q, k_cache, v_cache, block_tables, context_lens, q_lens, scale, num_kv_heads, block_size=16):
+    """The oracle's (out, lse), plus the same attention over |V|: per output element, the softmax-weighted
+    mean of |v| over the visible keys, which bounds what rounding the probabilities can move it by."""
+    out, lse = O.paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, q_lens, scale,
+                                        num_kv_heads, block_size)
+    vabs, _ = O.paged_decode_attention(q, k_cache, abs_values(v_cache), block_tables, context_lens, q_lens, scale,
+                                       num_kv_heads, block_size)
+    return out, lse, vabs
+
+
 def oracle_full(w: Workload, k_cache=None, v_cache=None):
+    """(out, lse, vabs) of the oracle on the whole workload (see oracle_with_vabs)."""
     kc = host_bits(w.k_cache if k_cache is None else k_cache)
     vc = host_bits(w.v_cache if v_cache is None else v_cache)
     kc, vc = _pools(w, kc, vc)
-    return O.paged_decode_attention(host_bits(w.q), kc, vc, w.block_tables, w.context_lens, w.q_lens,
-                                    w.scale, w.spec.num_kv_heads, w.spec.block_size)
+    return oracle_with_vabs(host_bits(w.q), kc, vc, w.block_tables, w.context_lens, w.q_lens, w.scale,
+                            w.spec.num_kv_heads, w.spec.block_size)
 
 
 def host_threads() -> int:
@@ -93,7 +111,8 @@ def oracle_all(w: Workload, k_cache=None, v_cache=None, seqs=None, threads=None)
     oracle_full call: each sequence is its own single-sequence oracle call over a host copy of just
     its pages (E4M3 pages decoded per sequence), and the calls are spread over host threads (numpy
     releases the GIL in its array work; BLAS runs one thread per call).  Rows of sequences not listed
-    stay NaN.  Returns (out [total_q, H, D], lse [total_q, H]) in float64, like oracle_full."""
+    stay NaN.  Returns (out [total_q, H, D], lse [total_q, H], vabs [total_q, H, D]) in float64, like
+    oracle_full."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
@@ -115,39 +134,45 @@ def oracle_all(w: Workload, k_cache=None, v_cache=None, seqs=None, threads=None)
     starts = np.concatenate([[0], np.cumsum(w.q_lens.astype(np.int64))])
     out = np.full((w.total_q, H, D), np.nan)
     lse = np.full((w.total_q, H), np.nan)
+    vabs = np.full((w.total_q, H, D), np.nan)
 
     def one(s):
         n, qs, b = int(w.context_lens[s]), int(w.q_lens[s]), int(starts[s])
         loc = remap[w.block_tables[s, :nblk[s]].astype(np.int64)]
         kc, vc = _pools(w, kc_h[loc], vc_h[loc])
         table = np.arange(nblk[s], dtype=np.int32)[None, :]
-        o, l = O.paged_decode_attention(q_h[b:b + qs], kc, vc, table, np.array([n], np.int32),
-                                        np.array([qs], np.int32), w.scale, w.spec.num_kv_heads, B)
+        o, l, a = oracle_with_vabs(q_h[b:b + qs], kc, vc, table, np.array([n], np.int32), np.array([qs], np.int32),
+                                   w.scale, w.spec.num_kv_heads, B)
         out[b:b + qs] = o
         lse[b:b + qs] = l
+        vabs[b:b + qs] = a
 
     with threadpool_limits(limits=1):
         with ThreadPoolExecutor(threads or host_threads()) as ex:
             list(ex.map(one, sorted(seqs, key=lambda s: -int(w.context_lens[s]) * int(w.q_lens[s]))))
-    return out, lse
+    return out, lse, vabs
 
 
 def tolerance(w: Workload) -> float:
     return F32_TOL if w.spec.dtype == "f32" else BF16_TOL
 
 
-# Diagnostic gate for bf16 outputs, far tighter than the 1.5e-2 bar: an output element may differ from
-# the oracle by its own bf16 rounding (at most |ref| 2^-9) plus the same again, plus 2e-3 for the
-# probabilities the value product multiplies in bf16.  A dropped key, a wrong scale or a misplaced
-# partial moves elements by much more at small |ref| long before the absolute bar trips.
-BF16_DIAG_REL = 2.0 ** -8
-BF16_DIAG_ABS = 2e-3
+# Diagnostic gate for bf16 outputs, far tighter than the 1.5e-2 bar.  With u = 2^-8 the unit roundoff
+# of bf16 (8 significant bits), a bf16 result may differ from the oracle by the rounding of the output
+# itself, at most u |ref|, plus the rounding of each probability to bf16 for the value product, at
+# most u p_t each, which moves the output by at most u sum_t w_t |v_t| = u vabs (w the softmax weights;
+# vabs is the oracle's attention over |V|).  The fp32 sums and the exp2 unit add far less than the
+# 1e-4 of slack.  A dropped key, a wrong scale or a misplaced partial at short or moderate contexts
+# moves elements by more than this long before the absolute bar trips.
+BF16_U = 2.0 ** -8
+BF16_DIAG_ABS = 1e-4
 
 
-def compare(w: Workload, out, lse, ref_out, ref_lse, rows=None):
+def compare(w: Workload, out, lse, ref_out, ref_lse, ref_vabs=None, rows=None):
     """Max |delta| of out and lse over the rows the oracle computed (NaN rows are skipped).  For bf16
-    outputs it also prints, and asserts, the diagnostic gate |delta| <= |ref| 2^-8 + 2e-3 element by
-    element, with the largest error beyond the output's own bf16 rounding (|delta| - |ref| 2^-9)."""
+    outputs it also prints, and asserts, the diagnostic gate |delta| <= u (|ref| + vabs) + 1e-4 element
+    by element (ref_vabs from oracle_with_vabs is then required), with the largest error beyond the
+    output's own bf16 rounding (|delta| - u |ref|)."""
     got = widen_out(out)
     mask = ~np.isnan(ref_out[:, 0, 0]) if rows is None else rows
     delta = np.abs(got[mask] - ref_out[mask])
@@ -157,10 +182,15 @@ def compare(w: Workload, out, lse, ref_out, ref_lse, rows=None):
         gl = lse.detach().cpu().numpy().astype(np.float64)
         d_lse = float(np.max(np.abs(gl[mask] - ref_lse[mask])))
     if out.dtype == torch.bfloat16:
-        mag = np.abs(ref_out[mask])
-        beyond = float(np.max(delta - mag * 2.0 ** -9))
-        slack = float(np.max(delta - (mag * BF16_DIAG_REL + BF16_DIAG_ABS)))
-        print(f"   bf16 diagnostic: beyond own rounding {beyond:.3e}, gate margin {-slack:.3e}", flush=True)
-        assert np.isfinite(slack) and slack <= 0.0, (
-            f"bf16 diagnostic gate |d| <= |ref| 2^-8 + 2e-3 exceeded by {slack:.3e}")
+        assert ref_vabs is not None, "bf16 comparisons need the oracle's attention over |V| (oracle_with_vabs)"
+        bf16_gate(delta, ref_out[mask], ref_vabs[mask])
     return d_out, d_lse
+
+
+def bf16_gate(delta, ref, vabs):
+    """Print and assert the bf16 diagnostic gate |delta| <= u (|ref| + vabs) + 1e-4, element by element."""
+    mag = np.abs(ref)
+    beyond = float(np.max(delta - mag * BF16_U))
+    use = float(np.max(delta / (BF16_U * (mag + vabs) + BF16_DIAG_ABS)))
+    print(f"   bf16 diagnostic: beyond own rounding {beyond:.3e}, gate use {use:.3f}", flush=True)
+    assert np.isfinite(use) and use <= 1.0, f"bf16 diagnostic gate |d| <= u (|ref| + vabs) + 1e-4 exceeded ({use:.3f}x)"

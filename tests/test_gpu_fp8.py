@@ -9,7 +9,7 @@ from oracle import paged_attention as O
 from paged_kv_cache_199_amd import _lib
 from paged_kv_cache_199_amd import workloads as W
 from tests.gpu_helpers import (BF16_TOL, LSE_TOL, compare, host_bits, nan_empty, nan_like, oracle_full,
-                               oracle_all, run_library)
+                               oracle_all, oracle_with_vabs, run_library)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -153,8 +153,8 @@ def _fp8_append_case(spec, label, variants=({},)):
                                       F.quantize(nv.float().cpu().numpy(), vs), slots)
     meta = w.device_meta(DEV)
     qlens = None if w.uniform_q else meta["q_lens"]
-    ref = O.paged_decode_attention(host_bits(w.q), F.dequantize(want_k, ks), F.dequantize(want_v, vs),
-                                   w.block_tables, w.context_lens, w.q_lens, w.scale, w.spec.num_kv_heads, B)
+    ref = oracle_with_vabs(host_bits(w.q), F.dequantize(want_k, ks), F.dequantize(want_v, vs), w.block_tables,
+                           w.context_lens, w.q_lens, w.scale, w.spec.num_kv_heads, B)
     for kw in variants:
         _say(f"[case] {label} fused append {kw}")
         kc, vc = w.k_cache.clone(), w.v_cache.clone()

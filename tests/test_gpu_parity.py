@@ -42,8 +42,8 @@ def _check_full(w, partition_size=0, variant=(_lib.PATH_AUTO, _lib.SCHEDULE_AUTO
     path, sched = variant
     _say(f"[case] {w.spec.name} P={partition_size} path={path} schedule={sched}")
     out, lse = run_library(w, DEV, partition_size=partition_size, path=path, schedule=sched)
-    ref_out, ref_lse = oracle_full(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
     assert np.isfinite(d_out) and d_out <= tolerance(w)
     assert np.isfinite(d_lse) and d_lse <= LSE_TOL
@@ -85,8 +85,8 @@ def test_spec_verify(gpu_lib):
         for variant in (MFMA_GRID, MFMA_PERSIST):
             _say(f"[case] spec_verify depth={depth} {variant}")
             out, lse = run_library(w, DEV, path=variant[0], schedule=variant[1], depth=depth)
-            ref_out, ref_lse = oracle_full(w)
-            d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+            ref_out, ref_lse, ref_vabs = oracle_full(w)
+            d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
             assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
 
@@ -99,14 +99,14 @@ def test_long_context_splitk_every_sequence(gpu_lib):
 
     w = W.build(4, DEV)
     t0 = time.perf_counter()
-    ref_out, ref_lse = oracle_all(w)
+    ref_out, ref_lse, ref_vabs = oracle_all(w)
     _say(f"   oracle on all {w.num_seqs} sequences ({int(w.context_lens.sum())} tokens): "
          f"{time.perf_counter() - t0:.1f} s on {host_threads()} host threads")
     assert not np.isnan(ref_out).any()
     for (path, sched), P in [(v, 512) for v in _paths(w)] + [(MFMA_PERSIST, 0)]:
         _say(f"[case] long_ctx_splitk_bf16 P={P} (full size, every row) path={path} schedule={sched}")
         out, lse = run_library(w, DEV, partition_size=P, path=path, schedule=sched)
-        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
         _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
         assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
@@ -115,8 +115,8 @@ def _check_persistent(w, P, depth):
     _say(f"[case] {w.spec.name} persistent P={P} depth={depth}")
     out, lse = run_library(w, DEV, partition_size=P, path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT,
                            depth=depth)
-    ref_out, ref_lse = oracle_full(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
     assert np.isfinite(d_out) and d_out <= BF16_TOL
     assert np.isfinite(d_lse) and d_lse <= LSE_TOL
@@ -187,8 +187,8 @@ def test_largest_batch_the_persistent_schedule_lists(gpu_lib, S):
     assert plan["schedule"] == (_lib.SCHEDULE_PERSISTENT if S <= 4096 else _lib.SCHEDULE_GRID)
     _say(f"[case] {S} sequences, schedule {plan['schedule']}")
     out, lse = run_library(w, DEV)
-    ref_out, ref_lse = oracle_full(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
@@ -209,8 +209,8 @@ def test_balanced_schedule_sequence_lookup_across_chunks(gpu_lib, S):
     assert plan["schedule"] == _lib.SCHEDULE_PERSISTENT
     _say(f"[case] {S} sequences, persistent schedule, {int(ctx.sum())} context tokens")
     out, lse = run_library(w, DEV)
-    ref_out, ref_lse = oracle_full(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
@@ -323,7 +323,7 @@ def test_workspace_reuse_across_calls(gpu_lib):
                                w.max_context_len, max_q_len=w.max_q_len, path=_lib.PATH_MFMA,
                                schedule=_lib.SCHEDULE_PERSISTENT, workspace=ws)
         torch.cuda.synchronize()
-        ref_out, ref_lse = oracle_full(w)
-        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+        ref_out, ref_lse, ref_vabs = oracle_full(w)
+        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
         _say(f"[case] workspace reuse {w.spec.name}: {d_out:.3e} {d_lse:.3e}")
         assert d_out <= BF16_TOL and d_lse <= LSE_TOL

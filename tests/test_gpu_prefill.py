@@ -35,9 +35,9 @@ def _prefill(w, ragged=None):
 def _check(spec, label, ragged=None):
     _say(f"[case] {label}")
     w = W.build(spec, DEV, poison=True)
-    ref_out, ref_lse = oracle_full(w)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
     out, lse = _prefill(w, ragged)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
@@ -75,9 +75,9 @@ def test_uniform_chunks_without_q_lens(gpu_lib):
 def test_chunked_prefill_workload_every_sequence(gpu_lib):
     w = W.build("prefill_chunk_bf16", DEV)
     _say(f"[case] prefill_chunk_bf16, every sequence ({w.total_q} new tokens)")
-    ref_out, ref_lse = oracle_all(w)
+    ref_out, ref_lse, ref_vabs = oracle_all(w)
     out, lse = _prefill(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 
@@ -95,8 +95,8 @@ def test_prefill_over_fp8_pools(gpu_lib, D):
 def test_prefill_fp8_workload_every_sequence(gpu_lib):
     w = W.build("prefill_chunk_fp8kv", DEV)
     _say(f"[case] prefill_chunk_fp8kv, every sequence ({w.total_q} new tokens)")
-    ref_out, ref_lse = oracle_all(w)
+    ref_out, ref_lse, ref_vabs = oracle_all(w)
     out, lse = _prefill(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"   max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL

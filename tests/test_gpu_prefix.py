@@ -42,9 +42,9 @@ def _run_prefix(w, groups, max_group_size=None, max_prefix_len=None, mode=_lib.P
 
 
 def _check(w, groups, label, **kw):
-    ref_out, ref_lse = oracle_full(w)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
     out, lse = _run_prefix(w, groups, **kw)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"[case] {label}: max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
     plain, plain_lse = run_library(w, DEV, k_cache=w.k_cache, v_cache=w.v_cache)
@@ -89,9 +89,9 @@ def test_system_prompt_batch_every_sequence(gpu_lib):
     # 64 sequences behind one 4096-token prefix (256 shared pages, 256 rows: eight row tiles)
     w = W.build("shared_prefix_64x4k_bf16", DEV)
     groups = W.share_prefixes(w, [(0, w.num_seqs, 4096)])
-    ref_out, ref_lse = oracle_all(w)
+    ref_out, ref_lse, ref_vabs = oracle_all(w)
     out, lse = _run_prefix(w, groups, mode=_lib.PREFIX_AUTO)      # the policy reads the prefix once here
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     _say(f"[case] shared_prefix_64x4k_bf16 every sequence: max|d out| = {d_out:.3e}  max|d lse| = {d_lse:.3e}")
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
 

@@ -46,8 +46,8 @@ def test_bound_step_matches_one_shot_calls_and_oracle(gpu_lib):
     # the append is in the cache, bit for bit
     want_k, want_v = O.kv_cache_write(kc0, vc0, host_bits(w.new_k), host_bits(w.new_v), w.slot_mapping)
     assert np.array_equal(host_bits(w.k_cache), want_k) and np.array_equal(host_bits(w.v_cache), want_v)
-    ref_out, ref_lse = oracle_full(w)
-    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
     print(f"[case] bound step: max|d out| {d_out:.3e} max|d lse| {d_lse:.3e}", flush=True)
     assert d_out <= BF16_TOL and d_lse <= LSE_TOL
     # the one-shot entry point on the same (already appended) cache gives the same bits

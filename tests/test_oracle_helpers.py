@@ -10,13 +10,16 @@ def test_threaded_per_sequence_oracle_equals_one_call():
     spec = W.custom("helpers", [1, 17, 300, 64, 1000, 33], q_len=[1, 2, 5, 1, 3, 4], num_heads=8, num_kv_heads=2,
                     head_dim=64)
     w = W.build(spec, "cpu", poison=True)
-    ref_out, ref_lse = oracle_full(w)
-    out, lse = oracle_all(w, threads=3)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    out, lse, vabs = oracle_all(w, threads=3)
     assert not np.isnan(out).any() and not np.isnan(lse).any()
     np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(vabs, ref_vabs, rtol=0, atol=1e-12)
+    # the attention over |V| bounds the output and is the attention of the same weights over |V|
+    assert (np.abs(ref_out) <= ref_vabs + 1e-12).all()
     # a subset leaves the other rows NaN
-    part, _ = oracle_all(w, seqs=[1, 4], threads=2)
+    part, _, _ = oracle_all(w, seqs=[1, 4], threads=2)
     starts = np.concatenate([[0], np.cumsum(w.q_lens)])
     for s in range(w.num_seqs):
         rows = part[starts[s]:starts[s + 1]]
@@ -27,7 +30,7 @@ def test_threaded_oracle_over_e4m3_pools():
     spec = W.custom("helpers_fp8", [5, 200, 47], q_len=[1, 3, 2], num_heads=4, num_kv_heads=2, head_dim=64,
                     kv_fp8=True)
     w = W.build(spec, "cpu")
-    ref_out, ref_lse = oracle_full(w)
-    out, lse = oracle_all(w, threads=2)
+    ref_out, ref_lse, ref_vabs = oracle_full(w)
+    out, lse, vabs = oracle_all(w, threads=2)
     np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
