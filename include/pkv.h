@@ -58,7 +58,10 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = -3, /* head_dim, block_size, dtype or partition size outside what is built */
   PKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than pkv_decode_workspace_bytes(); in
                                pkv_blocks.h: the block pool has too few free blocks */
-  PKV_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_SCRATCH = -6      /* pkv_paged_attn_decode_noalloc: the call needs more scratch than the
+                               library's static scratch holds (PKV_NOALLOC_SCRATCH_BYTES), or its
+                               address could not be found on this device */
 } pkv_status;
 
 /* PKV_BF16_FP8KV: q, out and appended rows bf16; the K and V pools hold 8-bit E4M3 codes (sign, 4-bit
@@ -219,6 +222,27 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
                                  int num_heads, int num_kv_heads, int head_dim, int block_size,
                                  float scale, int dtype, const pkv_decode_options *opts,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): pkv_paged_attn_decode without a workspace argument.  The split-K partials, spill
+ * rows and tables the decode keeps in its workspace go to a static device array of the library
+ * instead, PKV_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU the library runs on, held until the process
+ * ends.  Nothing is allocated: no hipMalloc / hipFree and no allocating library routine.  A call whose
+ * plan needs more scratch than that (pkv_decode_workspace_bytes() larger; e.g. fixed partitions over
+ * very long batches) returns PKV_ERR_SCRATCH and enqueues nothing.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (different streams, or host threads) race: serialize
+ * them.  The decode needs nothing in the scratch to start at zero.  Arguments, preconditions, results
+ * and the other errors are those of pkv_paged_attn_decode; the results are the same bits.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *q_lens, void *out, float *lse,
+                                  int num_seqs, int max_blocks_per_seq, int total_q, int max_q_len,
+                                  int max_context_len, int64_t num_blocks,
+                                  int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                  float scale, int dtype, const pkv_decode_options *opts, void *stream);
 
 /* Human-readable text for a pkv_status value (static storage): the error side of the boundary, which,
  * like the lfm25-inference page's runtime ("Runtime Design": an engine that owns its pages and

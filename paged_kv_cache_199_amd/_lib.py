@@ -52,6 +52,10 @@ EXPORTS = {
                                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                               _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                               ctypes.POINTER(DecodeOptions), _vp, _c_sz, _vp]),
+    "pkv_paged_attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                               _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
+                                               ctypes.POINTER(DecodeOptions), _vp]),
     "pkv_kv_cache_write_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_f,
                                         _vp]),
     "pkv_decode_shared_prefix_workspace_bytes": (_c_sz, [_c_int] * 11 + [ctypes.POINTER(DecodeOptions)]),
@@ -322,6 +326,31 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                                           float(scale), code, ctypes.byref(o), _ptr(workspace), ws_bytes,
                                           _stream(stream))
     _check(rc, "pkv_paged_attn_decode_append")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20     # PKV_NOALLOC_SCRATCH_BYTES in include/pkv.h
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor,
+                              q_lens: Optional[torch.Tensor], out: torch.Tensor, lse: Optional[torch.Tensor],
+                              num_heads: int, num_kv_heads: int, head_dim: int, block_size: int, scale: float,
+                              max_context_len: int, max_q_len: int = 1, partition_size: int = 0,
+                              path: int = PATH_AUTO, stream=None, depth: int = 0, schedule: int = 0,
+                              wgs_per_cu: int = 0, k_scale: float = 0.0, v_scale: float = 0.0) -> None:
+    """paged_attn_decode for callers that cannot allocate (pkv_paged_attn_decode_noalloc): the library's
+    static per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace, and nothing is allocated here
+    or in the library.  Calls that overlap on one GPU share that scratch and race."""
+    lib = load()
+    total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                                              num_heads, num_kv_heads, head_dim, block_size)
+    o = _opts(partition_size, path, None, depth, schedule, wgs_per_cu, k_scale, v_scale)
+    rc = lib.pkv_paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                           _ptr(context_lens), _ptr(q_lens), _ptr(out), _ptr(lse),
+                                           S, block_tables.shape[1], total_q, max_q_len, max_context_len, NB,
+                                           num_heads, num_kv_heads, head_dim, block_size, float(scale), code,
+                                           ctypes.byref(o), _stream(stream))
+    _check(rc, "pkv_paged_attn_decode_noalloc")
 
 
 def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,

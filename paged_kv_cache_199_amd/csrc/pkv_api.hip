@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "decode_args.h"
 
 namespace pkv {
@@ -220,6 +222,9 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype, path or partition size";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small, or too few free blocks";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_SCRATCH:
+      return "the call needs more than the library's static decode scratch (PKV_NOALLOC_SCRATCH_BYTES), "
+             "or its device address was not found";
     default: return "unknown status";
   }
 }
@@ -418,6 +423,60 @@ int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cach
   return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
                      num_seqs, max_blocks_per_seq, total_q, max_q_len, max_context_len, num_blocks, num_heads,
                      num_kv_heads, head_dim, block_size, scale, dtype, opts, workspace, workspace_bytes,
+                     stream);
+}
+
+}  // extern "C"
+
+// Static decode scratch of pkv_paged_attn_decode_noalloc: one copy per GPU, owned by the library until
+// the process ends.  In host code `scratch` names a host-side stand-in, not device memory: its device
+// address on the current GPU comes from hipGetSymbolAddress, taken once per device and kept.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, or nullptr.
+void *scratch_on_current_device() {
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *q_lens, void *out, float *lse, int num_seqs,
+                                  int max_blocks_per_seq, int total_q, int max_q_len, int max_context_len,
+                                  int64_t num_blocks, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, float scale, int dtype, const pkv_decode_options *opts,
+                                  void *stream) {
+  // the decode's own validation first, so a bad call fails the same way as pkv_paged_attn_decode
+  if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  const int st = shape_status(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                              head_dim, dtype, opts);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                            dtype, q_lens != nullptr, opts);
+  if (pl.bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  void *ws = scratch_on_current_device();
+  if (!ws) return PKV_ERR_SCRATCH;
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
+                     num_seqs, max_blocks_per_seq, total_q, max_q_len, max_context_len, num_blocks, num_heads,
+                     num_kv_heads, head_dim, block_size, scale, dtype, opts, ws, PKV_NOALLOC_SCRATCH_BYTES,
                      stream);
 }
 

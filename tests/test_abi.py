@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pkv_version() >> 16 == 1
-    for code in range(-5, 1):
+    for code in range(-6, 1):
         assert lib.pkv_status_string(code)
     assert lib.pkv_status_string(-99) == b"unknown status"
 
