@@ -243,11 +243,29 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 template <bool F8> struct KvRaw {
   typedef uint4 K;      // 8 bf16 of one token row: the score product's A operand
   typedef uint2 V;      // 4 tokens of one dim: the value product's A operand
+  static constexpr int VT = 1;   // value-product tiles (16 dims each) per V register
 };
+// E4M3 pages are read with 16-byte loads: the vector-memory address unit spends about the same time on a
+// load whatever its width, and with the 4-byte loads that the value operand's layout asks for (4 codes
+// of one dim per lane) it, not HBM, bounded the E4M3 decode (busy ~95% of the kernel with few memory
+// stalls).  So a lane loads a whole 16-token dim row and a transpose across the wave's four 16-lane
+// rows hands each lane its 4 codes of each of 4 tiles.
 template <> struct KvRaw<true> {
   typedef uint2 K;      // 8 E4M3 codes
-  typedef uint32_t V;   // 4 E4M3 codes
+  typedef uint4 V;      // lane (c, r): dim row 64 h + 16 r + c (16 tokens) as loaded
+  static constexpr int VT = 4;
 };
+
+// 4x4 transpose of 32-bit words across the four 16-lane rows of the wave (every lane active): lane
+// (c, r), holding words A[r][0..3], ends with A[t][r] as its word t.  Two rounds of gfx950's lane swaps:
+// between the 32-lane halves (words 0/2 and 1/3), then between neighbouring 16-lane rows (0/1, 2/3).
+__device__ __forceinline__ uint4 transpose_rows4(uint4 v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return make_uint4(c[0], c[1], d[0], d[1]);
+}
 
 template <int D>
 __device__ __forceinline__ void widen_page(const uint4 *kin, const uint2 *vin, uint4 *kout, uint2 *vout) {
@@ -257,13 +275,20 @@ __device__ __forceinline__ void widen_page(const uint4 *kin, const uint2 *vin, u
   for (int t = 0; t < D / 16; ++t) vout[t] = vin[t];
 }
 template <int D>
-__device__ __forceinline__ void widen_page(const uint2 *kin, const uint32_t *vin, uint4 *kout, uint2 *vout) {
+__device__ __forceinline__ void widen_page(const uint2 *kin, const uint4 *vin, uint4 *kout, uint2 *vout) {
   #pragma unroll
   for (int c = 0; c < D / 32; ++c)
     kout[c] = make_uint4(fp8x2_to_bf16x2<false>(kin[c].x), fp8x2_to_bf16x2<true>(kin[c].x),
                          fp8x2_to_bf16x2<false>(kin[c].y), fp8x2_to_bf16x2<true>(kin[c].y));
   #pragma unroll
-  for (int t = 0; t < D / 16; ++t) vout[t] = make_uint2(fp8x2_to_bf16x2<false>(vin[t]), fp8x2_to_bf16x2<true>(vin[t]));
+  for (int h = 0; h < D / 64; ++h) {
+    // word t of lane (c, r): codes of tokens 4 r .. 4 r + 3 of dim 64 h + 16 t + c, i.e. tile 4 h + t
+    const uint4 w = transpose_rows4(vin[h]);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    #pragma unroll
+    for (int t = 0; t < 4; ++t)
+      vout[4 * h + t] = make_uint2(fp8x2_to_bf16x2<false>(ws[t]), fp8x2_to_bf16x2<true>(ws[t]));
+  }
 }
 
 // F8: the pools hold E4M3 codes (1 byte per element) instead of bf16; pages are half as large and are
@@ -292,8 +317,9 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   const int last = je - 1;
   auto id_of = [&](int j) -> int { return btc[__builtin_amdgcn_readfirstlane(min(j, last))]; };
 
+  constexpr int NV = ND / KvRaw<F8>::VT;   // V registers per page
   KR kb[NBUF][NK];
-  VR vb[NBUF][ND];
+  VR vb[NBUF][NV];
   bool okb[NBUF];
   auto issue = [&](int bid, KR *kr, VR *vr, bool &ok) {
     ok = bid >= 0 && bid < nb;
@@ -301,9 +327,16 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
     const char *kp = kbase + off + col * ROWB + grp * 8 * EB;
     #pragma unroll
     for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const KR *>(kp + c * 32 * EB);
-    const char *vp = vbase + off + (col * kBlock + 4 * grp) * EB;
-    #pragma unroll
-    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
+    if constexpr (F8) {
+      // whole dim rows: lane (col, grp) reads row 64 h + 16 grp + col
+      const char *vp = vbase + off + (16 * grp + col) * kBlock * EB;
+      #pragma unroll
+      for (int h = 0; h < NV; ++h) vr[h] = *reinterpret_cast<const VR *>(vp + h * 64 * kBlock * EB);
+    } else {
+      const char *vp = vbase + off + (col * kBlock + 4 * grp) * EB;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
+    }
   };
   // widen (E4M3) or take (bf16) page b of the ring, then substitute appended tokens, then compute
   auto compute = [&](int j, const KR *kr, const VR *vr, bool ok) {

@@ -22,7 +22,8 @@ __global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict
   constexpr int NK = D / 32;
   constexpr int ND = D / 16;
   typedef typename std::conditional<F8, uint2, uint4>::type KR;      // 8 elements of a K row
-  typedef typename std::conditional<F8, uint32_t, uint2>::type VR;   // 4 tokens of a V dim
+  typedef typename std::conditional<F8, uint4, uint2>::type VR;      // 4 tokens of a V dim (E4M3: a dim row)
+  constexpr int NV = F8 ? ND / 4 : ND;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -40,20 +41,27 @@ __global__ __launch_bounds__(256) void page_stream_kernel(const char *__restrict
   };
   uint32_t acc = 0;
   KR kb[NBUF][NK];
-  VR vb[NBUF][ND];
+  VR vb[NBUF][NV];
   auto issue = [&](int64_t id, KR *kr, VR *vr) {
     const char *kp = K + id * page_bytes + col * ROWB + grp * 8 * EB;
     #pragma unroll
     for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const KR *>(kp + c * 32 * EB);
-    const char *vp = V + id * page_bytes + (col * kBlock + 4 * grp) * EB;
-    #pragma unroll
-    for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
+    if constexpr (F8) {
+      // E4M3 pages: whole 16-token dim rows, lane (col, grp) reading row 64 h + 16 grp + col
+      const char *vp = V + id * page_bytes + (16 * grp + col) * kBlock * EB;
+      #pragma unroll
+      for (int h = 0; h < NV; ++h) vr[h] = *reinterpret_cast<const VR *>(vp + h * 64 * kBlock * EB);
+    } else {
+      const char *vp = V + id * page_bytes + (col * kBlock + 4 * grp) * EB;
+      #pragma unroll
+      for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const VR *>(vp + t * 16 * kBlock * EB);
+    }
   };
   auto use = [&](const KR *kr, const VR *vr) {
     #pragma unroll
     for (int c = 0; c < NK; ++c) acc += kr[c].x ^ kr[c].y;
     #pragma unroll
-    for (int t = 0; t < ND; ++t) acc += reinterpret_cast<const uint32_t *>(&vr[t])[0];
+    for (int t = 0; t < NV; ++t) acc += reinterpret_cast<const uint32_t *>(&vr[t])[0];
   };
   int64_t sid[NBUF];
   #pragma unroll
