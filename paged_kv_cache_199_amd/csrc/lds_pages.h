@@ -209,16 +209,26 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
     for (int p = 0; p < SP; ++p) {
       if (p >= p0 && p < p1 && j0 + p < jw) {
         const char *pg = src + p * L::PBYTES;
+        // the lane's LDS offsets are recomputed on every page (a few integer operations) rather than
+        // kept live across the walk: at this register budget the compiler spilled them, and each
+        // reload waited on every load in flight, the next stage's included
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int cl = ln & 15;
+        const int gl = ln >> 4;
         uint4 kr[NK];
         uint2 vr[ND];
         #pragma unroll
         for (int c = 0; c < NK; ++c)
-          kr[c] = *reinterpret_cast<const uint4 *>(pg + col * (D * 2) + (((4 * c + grp) ^ col) * 16));
+          kr[c] = *reinterpret_cast<const uint4 *>(pg + cl * (D * 2) + (((4 * c + gl) ^ cl) * 16));
+        const int voff = cl * (kBlock * 2) + ((gl >> 1) ^ ((cl >> 2) & 1)) * 16 + (gl & 1) * 8;
         #pragma unroll
         for (int t = 0; t < ND; ++t) {
-          const int d = col + 16 * t;
-          vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + d * (kBlock * 2) +
-                                                   ((((grp >> 1) ^ ((d >> 2) & 1)) * 16) + (grp & 1) * 8));
+          // one address register per read keeps the reads apart (merged pairs lost track of which LDS
+          // buffer they read, and waited for the loads into the other one)
+          int vo = voff + t * 16 * (kBlock * 2);
+          asm volatile("" : "+v"(vo));
+          vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + vo);
         }
         mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
       }
