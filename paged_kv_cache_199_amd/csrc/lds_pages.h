@@ -170,8 +170,6 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
   const int n = je - jb;
   if (n <= 0) return;
   const int nstages = (n + SP - 1) / SP;
@@ -184,13 +182,20 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const int k_off = kr_row * (D * 2) + (((lane & 15) ^ kr_row) * 16);
   const int vd = 32 * wave + (lane >> 1);
   const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> 2) & 1)) * 16);
-  // issue stage g's loads into buffer dst; returns bit p set when page p has a valid block id
-  auto fetch = [&](int g, char *dst) -> int {
+  // block ids of the next stage to fetch (lane p: page p), read one stage ahead and issued after a
+  // stage's global-to-LDS loads, so the stage-end wait covers both and no fetch waits for an id (read
+  // when needed, the id's wait would also count the loads in flight)
+  int idv = 0;
+  auto ids_of = [&](int g) {
+    idv = bt[jb + min(g * SP + min(lane, SP - 1), n - 1)];   // past the end: the last page
+  };
+  // issue the loads of the stage whose ids are in idv into buffer dst; returns bit p set when page p
+  // has a valid block id
+  auto fetch = [&](char *dst) -> int {
     int okn = 0;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      const int j = jb + min(g * SP + p, n - 1);     // past the end: re-read the last page
-      const int bid = bt[j];
+      const int bid = __builtin_amdgcn_readlane(idv, p);
       const bool ok = bid >= 0 && bid < a.num_blocks;
       okn |= ok ? 1 << p : 0;
       const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
@@ -200,14 +205,14 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
       __builtin_amdgcn_global_load_lds(vbase + page + v_off,
                                        (__attribute__((address_space(3))) void *)(pg + L::KBYTES + wave * 1024), 16, 0, 0);
     }
-    return __builtin_amdgcn_readfirstlane(okn);
+    return okn;
   };
-  // compute pages [p0, p1) of stage g from buffer src
-  auto compute = [&](int g, const char *src, int ok_bits, int p0, int p1) {
+  // compute the pages of stage g from buffer src
+  auto compute = [&](int g, const char *src, int ok_bits) {
     const int j0 = jb + g * SP;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      if (p >= p0 && p < p1 && j0 + p < jw) {
+      if (j0 + p < jw) {
         const char *pg = src + p * L::PBYTES;
         // the lane's LDS offsets are recomputed on every page (a few integer operations) rather than
         // kept live across the walk: at this register budget the compiler spilled them, and each
@@ -235,25 +240,24 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
     }
   };
 
-  int ok0 = fetch(0, buf0);
+  ids_of(0);
+  int ok0 = fetch(buf0);
+  if (nstages > 1) ids_of(1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int g = 0; g < nstages; g += 2) {
     // even stage from buf0 while the next one lands in buf1
-    // (the next stage's loads are issued after this stage's first page: at three waves per SIMD the
-    // page step spills a register whose reload waits on every load in flight, and the first page
-    // holds it)
     int ok1 = 0;
-    compute(g, buf0, ok0, 0, 1);
-    if (g + 1 < nstages) ok1 = fetch(g + 1, buf1);
-    compute(g, buf0, ok0, 1, SP);
+    if (g + 1 < nstages) ok1 = fetch(buf1);
+    if (g + 2 < nstages) ids_of(g + 2);
+    compute(g, buf0, ok0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads into buf1 have landed
     __syncthreads();
     if (g + 1 >= nstages) break;
     // odd stage from buf1 while the next one lands in buf0
-    compute(g + 1, buf1, ok1, 0, 1);
-    if (g + 2 < nstages) ok0 = fetch(g + 2, buf0);
-    compute(g + 1, buf1, ok1, 1, SP);
+    if (g + 2 < nstages) ok0 = fetch(buf0);
+    if (g + 3 < nstages) ids_of(g + 3);
+    compute(g + 1, buf1, ok1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
