@@ -144,9 +144,9 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
 // bf16 pools, D = 128: the same page walk with each stage fetched by gfx950's global-to-LDS loads
 // (global_load_lds_dwordx4), so no VGPRs hold pages in flight.  Such a load writes 16 bytes per lane
 // to consecutive LDS addresses (lane l at base + 16 l); each lane picks the global 16-byte chunk
-// that belongs there.  Page layout in LDS (8 KB): K as 16 token rows of 256 bytes, chunk c of row r
-// stored at position c ^ r (the 16 rows one K read touches then fall in different banks); V as 128
-// dim rows of 32 bytes (16 tokens), the two chunks of a row swapped where bit 2 of the dim is set
+// that belongs there.  Page layout in LDS (8 KB): K as four 1 KB blocks of 4 token rows, each row's
+// 16-byte chunks placed so that a lane's score operands share one base address (below), with the 16
+// rows one K read touches in different banks; V as 128 dim rows of 32 bytes (16 tokens), the two chunks of a row swapped where bit 2 of the dim is set
 // (2-way bank conflicts on V reads, the least that 16-byte chunks allow).  Two stage buffers are
 // separate LDS arrays, and the walk alternates between them with the buffer known at compile time,
 // so the compiler sees that reads of one never wait for loads into the other.
@@ -177,9 +177,12 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const char *vbase = static_cast<const char *>(a.v_cache);
   constexpr int64_t page_bytes = (int64_t)kBlock * D * 2;
   // this lane's chunk of the 1 KB K block (rows 4 wave .. + 3) and V block (dims 32 wave .. + 31)
-  // that its wave moves for every page
-  const int kr_row = 4 * wave + (lane >> 4);
-  const int k_off = kr_row * (D * 2) + (((lane & 15) ^ kr_row) * 16);
+  // that its wave moves for every page.  K block b holds, in 16-byte slot 16 c + 4 ((b + g) & 3) + j,
+  // chunk 4 c + g of token row 4 b + j: a lane's four score operands (chunks 4 c + g of its row, c <
+  // 4) are then 256 bytes apart, one base address and immediate offsets, and the 16 rows one read
+  // touches sit in 16 different bank groups
+  const int k_slot_g = ((lane >> 2) - wave) & 3;
+  const int k_off = (4 * wave + (lane & 3)) * (D * 2) + (4 * (lane >> 4) + k_slot_g) * 16;
   const int vd = 32 * wave + (lane >> 1);
   const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> 2) & 1)) * 16);
   // block ids of the next stage to fetch (lane p: page p), read one stage ahead and issued after a
@@ -210,31 +213,29 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   // compute the pages of stage g from buffer src
   auto compute = [&](int g, const char *src, int ok_bits) {
     const int j0 = jb + g * SP;
+    // the lane's two LDS base offsets, recomputed per stage rather than kept live across the walk: at
+    // this register budget the compiler spilled them, and each reload waited on every load in flight,
+    // the next stage's included
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int cl = ln & 15;
+    const int gl = ln >> 4;
+    const int kb = (cl >> 2) * 1024 + ((((cl >> 2) + gl) & 3) * 4 + (cl & 3)) * 16;
+    const int vb = cl * (kBlock * 2) + ((gl >> 1) ^ ((cl >> 2) & 1)) * 16 + (gl & 1) * 8;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
       if (j0 + p < jw) {
         const char *pg = src + p * L::PBYTES;
-        // the lane's LDS offsets are recomputed on every page (a few integer operations) rather than
-        // kept live across the walk: at this register budget the compiler spilled them, and each
-        // reload waited on every load in flight, the next stage's included
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        const int cl = ln & 15;
-        const int gl = ln >> 4;
         uint4 kr[NK];
         uint2 vr[ND];
         #pragma unroll
-        for (int c = 0; c < NK; ++c)
-          kr[c] = *reinterpret_cast<const uint4 *>(pg + cl * (D * 2) + (((4 * c + gl) ^ cl) * 16));
-        const int voff = cl * (kBlock * 2) + ((gl >> 1) ^ ((cl >> 2) & 1)) * 16 + (gl & 1) * 8;
+        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(pg + kb + c * 256);
+        // volatile keeps the value reads unmerged: a merged pair lost track of which LDS buffer it
+        // read, and waited for the loads into the other one
         #pragma unroll
-        for (int t = 0; t < ND; ++t) {
-          // one address register per read keeps the reads apart (merged pairs lost track of which LDS
-          // buffer they read, and waited for the loads into the other one)
-          int vo = voff + t * 16 * (kBlock * 2);
-          asm volatile("" : "+v"(vo));
-          vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + vo);
-        }
+        for (int t = 0; t < ND; ++t)
+          vr[t] = __builtin_bit_cast(uint2, *reinterpret_cast<const volatile uint64_t *>(pg + L::KBYTES + vb +
+                                                                                          t * 16 * (kBlock * 2)));
         mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
       }
     }
