@@ -121,11 +121,17 @@ __device__ __forceinline__ void mfma_page(const DecodeArgs &a, const SeqInfo &si
       }
     }
   }
-  // lazy running max: moves only when a score exceeds it by more than kRescaleSlack
-  bool need = false;
+  // lazy running max: moves only when a score exceeds it by more than kRescaleSlack.  x is never NaN
+  // (masked scores are -inf), and for a threshold >= 0 a float exceeds it exactly when its bits, read
+  // as a signed integer, do: integer maxima need no NaN quieting, which float maxima pay per operand
+  static_assert(kRescaleSlack >= 0.f, "the integer comparison needs a non-negative threshold");
+  int xbits = __float_as_int(x[0][0]);
   #pragma unroll
-  for (int n = 0; n < NT; ++n)
-    need |= fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])) > kRescaleSlack;
+  for (int n = 0; n < NT; ++n) {
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) xbits = max(xbits, __float_as_int(x[n][e]));
+  }
+  const bool need = xbits > __float_as_int(kRescaleSlack);
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
     #pragma unroll
     for (int n = 0; n < NT; ++n) {
