@@ -230,12 +230,8 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
         uint2 vr[ND];
         #pragma unroll
         for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(pg + kb + c * 256);
-        // volatile keeps the value reads unmerged: a merged pair lost track of which LDS buffer it
-        // read, and waited for the loads into the other one
         #pragma unroll
-        for (int t = 0; t < ND; ++t)
-          vr[t] = __builtin_bit_cast(uint2, *reinterpret_cast<const volatile uint64_t *>(pg + L::KBYTES + vb +
-                                                                                          t * 16 * (kBlock * 2)));
+        for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + vb + t * 16 * (kBlock * 2));
         mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
       }
     }
