@@ -146,10 +146,12 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
 // to consecutive LDS addresses (lane l at base + 16 l); each lane picks the global 16-byte chunk
 // that belongs there.  Page layout in LDS (8 KB): K as four 1 KB blocks of 4 token rows, each row's
 // 16-byte chunks placed so that a lane's score operands share one base address (below), with the 16
-// rows one K read touches in different banks; V as 128 dim rows of 32 bytes (16 tokens), the two chunks of a row swapped where bit 2 of the dim is set
-// (2-way bank conflicts on V reads, the least that 16-byte chunks allow).  Two stage buffers are
-// separate LDS arrays, and the walk alternates between them with the buffer known at compile time,
-// so the compiler sees that reads of one never wait for loads into the other.
+// rows one K read touches in different banks; V as 128 dim rows of 32 bytes (16 tokens), the two
+// chunks of a row swapped where bit 2 of the dim is set (2-way bank conflicts on V reads, the least
+// that 16-byte chunks allow).  Two stage buffers are separate LDS arrays, and the walk alternates
+// between them with the buffer known at compile time, so the compiler sees that reads of one never
+// wait for loads into the other (with a third buffer it no longer does, and waits for every load in
+// flight before each page's reads).
 template <int SP>
 struct DmaPages {
   static constexpr int D = 128;
