@@ -227,7 +227,7 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
  * For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): pkv_paged_attn_decode without a workspace argument.  The split-K partials, spill
  * rows and tables the decode keeps in its workspace go to a static device array of the library
- * instead, PKV_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU the library runs on, held until the process
+ * instead, PKV_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on, held until the process
  * ends.  Nothing is allocated: no hipMalloc / hipFree and no allocating library routine.  A call whose
  * plan needs more scratch than that (pkv_decode_workspace_bytes() larger; e.g. fixed partitions over
  * very long batches) returns PKV_ERR_SCRATCH and enqueues nothing.  Every call on one GPU shares that
@@ -235,7 +235,7 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
  * them.  The decode needs nothing in the scratch to start at zero.  Arguments, preconditions, results
  * and the other errors are those of pkv_paged_attn_decode; the results are the same bits.
  */
-#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int pkv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *block_tables, const int32_t *context_lens,
                                   const int32_t *q_lens, void *out, float *lse,

@@ -328,7 +328,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check(rc, "pkv_paged_attn_decode_append")
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20     # PKV_NOALLOC_SCRATCH_BYTES in include/pkv.h
+NOALLOC_SCRATCH_BYTES = 64 << 20     # PKV_NOALLOC_SCRATCH_BYTES in include/pkv.h
 
 
 def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

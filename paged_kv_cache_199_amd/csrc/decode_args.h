@@ -42,6 +42,13 @@ struct DecodeArgs {
   int cut_align;               // share boundaries inside a work item fall on multiples of this
   int item_cost;               // pages of stream charged to each work item's start (its pipeline restart)
   int rows_per_tile;
+  // balanced schedule without fixed partitions: piece k < max_pieces of a work item (in stream order,
+  // piece 0 at the item's start) leaves its partial in partition row k, later pieces in their wave's
+  // spill rows, and the piece that ends an item writes the item's piece count to item_cnt
+  // (max_pieces + 1 when there are more).  The merge then finds a row's sources with no search.
+  // 0: no such slots (fixed partitions, grid schedule).
+  int max_pieces;
+  int32_t *item_cnt;           // [num_seqs][num_kv_heads][row_tiles]
   // append in the same pass: the new tokens' K/V rows, [total_q, num_kv_heads, head_dim] packed like
   // q; NULL when nothing is appended
   const void *new_k;
@@ -136,13 +143,29 @@ __device__ __forceinline__ int64_t share_raw(int64_t L, int NW, int ord) {
   return (int64_t)floor((double)L * (double)ord / (double)NW);
 }
 
-// Smallest share whose raw start lies above pos, for 0 <= pos < L: the double estimate of
-// ceil((pos + 1) NW / L) is at most one below it; step up with exact comparisons.
+// Smallest share whose raw start lies above pos (NW when none does, pos >= 0).  floor(L c / NW) > pos
+// exactly when L c >= (pos + 1) NW = t, so the answer is ceil(t / L) when t < L NW.  There t / L < NW
+// <= 2^13, and the single-precision quotient (three roundings, each within 2^-24 relative) is within
+// 2^-9 of it: its integer part is at most two below the answer and never above it.  Exact integer
+// products settle it (the downward step only guards that bound).
 __device__ __forceinline__ int first_share_above(int64_t L, int NW, int64_t pos) {
-  int c = (int)floor((double)(pos + 1) * (double)NW / (double)L) - 1;
-  c = max(c, 0);
-  while (c < NW && share_raw(L, NW, c) <= pos) ++c;
+  const int64_t t = (pos + 1) * NW;
+  if (t >= L * NW) return NW;
+  int c = min(max((int)((float)t / (float)L), 0), NW);
+  while ((int64_t)c * L < t) ++c;
+  while (c > 0 && (int64_t)(c - 1) * L >= t) --c;
   return c;
+}
+
+// Piece index, within its work item, of the piece that share o starts inside the item's real pages
+// (no fixed partitions).  The item occupies stream [pos0, pos0 + C + nblk); piece 0 starts at the
+// item's start.  When every share holds at least one page of stream (L >= NW), every share whose raw
+// start lies past the item's C virtual pages starts one more piece, so share o's piece is o minus the
+// first such share, plus one.  Otherwise shares can be empty, and cap is returned: those pieces take
+// their wave's spill rows and the merge searches for them.  The result is capped at cap.
+__device__ __forceinline__ int piece_index(int64_t L, int NW, int C, int64_t pos0, int o, int cap) {
+  if (L < NW) return cap;
+  return min(o - first_share_above(L, NW, pos0 + C) + 1, cap);
 }
 
 // Workgroup-wave slot of share ord: workgroup (wx / 4) * 8 + x, wave wx % 4.

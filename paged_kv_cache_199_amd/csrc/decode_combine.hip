@@ -59,10 +59,77 @@ __device__ __forceinline__ void merge_prefix_chunks(const DecodeArgs &a, const P
   if (lane == 0 && a.lse) a.lse[base] = (mx + log2_hw(wsum)) * kLn2;
 }
 
-template <bool BF16, int D, bool PRE>
+// With piece slots on and the same number of new tokens in every sequence, a row's position and its
+// work item follow from (s, i, h) alone, and its first pieces sit in partition rows 0 .. max_pieces - 1:
+// the item's piece count and the partials of all its slots are requested before any of them returns,
+// one round trip where the general merge takes two (the lengths, then the sources).  The slots past
+// the count are read for nothing; with few rows that costs less than waiting for the count first
+// (measured on the concurrency-32, shared-prefix and E4M3 batches).  Returns false when the item has
+// more pieces than NS (the general merge takes over).
+template <bool BF16, int D, int NS>
+__device__ __forceinline__ bool merge_slots(const DecodeArgs &a, int s, int i, int h, int lane) {
+  constexpr int DPL = D / 64;
+  const int H = a.num_heads;
+  const int G = a.group;
+  const int kvh = h / G;
+  const int rt = (i * G + h - kvh * G) / a.rows_per_tile;
+  const int row = s * a.max_q_len + i;
+  const int64_t stride = (int64_t)a.total_q * H;
+  const int64_t base = (int64_t)row * H + h;
+  const int mp = a.max_pieces;
+  const int ctx_raw = a.context_lens[s];
+  const int cnt = a.item_cnt[((int64_t)s * a.num_kv_heads + kvh) * a.row_tiles + rt];
+  const float l = lane < mp && lane < NS ? a.part_lse[lane * stride + base] : -INFINITY;
+  float v[NS][DPL];
+  #pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const float *op = a.part_o + ((int64_t)u * stride + base) * D + lane;
+    #pragma unroll
+    for (int k = 0; k < DPL; ++k) v[u][k] = u < mp ? op[64 * k] : 0.f;
+  }
+  // the row's validity, clamped as the partition pass clamps it
+  int ctx = min(min(ctx_raw, a.max_context_len), a.max_blocks_per_seq * kBlock);
+  ctx = max(ctx, 0);
+  const int qs = max(1, min(a.max_q_len, ctx));
+  if (i >= qs || ctx <= 0 || row >= a.total_q) return true;
+  if (cnt <= 1) return true;                // one piece: the partition pass wrote the final row
+  if (cnt > NS || cnt > mp) return false;
+  const float ls = lane < cnt ? l : -INFINITY;
+  const float M = wave_max(ls);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  const float wl = ls == -INFINITY ? 0.f : exp2_hw(ls - Ms);
+  float acc[DPL];
+  #pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+  #pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const float wp = __shfl(wl, u);
+    #pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = u < cnt ? fmaf(wp, v[u][k], acc[k]) : acc[k];   // slots past cnt hold anything
+  }
+  const float L2 = wave_sum(wl);
+  const bool seen = L2 > 0.f;
+  const float inv = seen ? 1.f / L2 : 0.f;
+  #pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const float o = acc[k] * inv;
+    if constexpr (BF16) {
+      static_cast<uint16_t *>(a.out)[base * D + lane + 64 * k] = f32_to_bf16(o);
+    } else {
+      static_cast<float *>(a.out)[base * D + lane + 64 * k] = o;
+    }
+  }
+  if (lane == 0 && a.lse) a.lse[base] = seen ? (Ms + log2_hw(L2)) * kLn2 : -INFINITY;
+  return true;
+}
+
+template <bool BF16, int D, bool PRE, int NS = 0>
 __device__ __forceinline__ void combine_row(const DecodeArgs &a, const PrefixArgs &p, int s, int i, int h, int lane) {
   constexpr int DPL = D / 64;
   const int H = a.num_heads;
+  if constexpr (NS > 0 && !PRE) {
+    if (merge_slots<BF16, D, NS>(a, s, i, h, lane)) return;
+  }
   // issued before the sequence's lengths come back: they do not depend on them
   const bool spill = a.spill_base >= 0;
   const int pre_s = spill ? a.item_pre[s] : 0;
@@ -136,7 +203,10 @@ __device__ __forceinline__ void combine_row(const DecodeArgs &a, const PrefixArg
     const int64_t bn = share_raw(L, NW, ord + 1);
     const int obn = bn < pos1 ? real_off(bn) : nblk;
     if (obn <= ob) return false;
-    prow = a.spill_base + (int64_t)share_slot(W, ord) * a.rows_per_tile + srow;
+    // piece slots on (then there is one partition): pieces below max_pieces sit in partition rows
+    const int kp = a.max_pieces > 1 ? piece_index(L, NW, C, pos0, ord, a.max_pieces) : a.max_pieces;
+    prow = kp < a.max_pieces ? kp * stride + base
+                             : a.spill_base + (int64_t)share_slot(W, ord) * a.rows_per_tile + srow;
     return true;
   };
   const int nsrc = si.nparts + ncand;
@@ -269,16 +339,60 @@ __device__ __forceinline__ void combine_row(const DecodeArgs &a, const PrefixArg
   if (lane == 0 && a.lse) a.lse[base] = seen ? (Ms + log2_hw(L2)) * kLn2 : -INFINITY;
 }
 
-template <bool BF16, int D, bool PRE>
+// NS > 0: piece slots on and uniform new tokens; the first NS slots are read in the first round trip.
+template <bool BF16, int D, bool PRE, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, PrefixArgs p) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int H = a.num_heads;
   const int64_t nw = (int64_t)a.num_seqs * a.max_q_len * H;
   if (wid >= nw) return;
   const int h = (int)(wid % H);
   const int64_t t = wid / H;
-  combine_row<BF16, D, PRE>(a, p, (int)(t / a.max_q_len), (int)(t % a.max_q_len), h, lane);
+  combine_row<BF16, D, PRE, NS>(a, p, (int)(t / a.max_q_len), (int)(t % a.max_q_len), h, lane);
+}
+
+// The G rows' merge once the sources are known: lane j G + hg holds source j's log2 LSE l for head hg
+// (-inf: not a source), v[u] this lane's E floats of source u's G x D block (anything past nsrc).
+template <bool BF16, int D, int E>
+__device__ __forceinline__ void group_merge(const DecodeArgs &a, int64_t base, int lane, float l,
+                                            const float4_v v[][E / 4], int nsrc) {
+  constexpr int G = E * 64 / D;
+  constexpr int LG = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
+  const int e0 = lane * E;
+  const int hgd = e0 / D;
+  // per-head max and weight sum over the sources: lanes hg, hg + G, hg + 2G, ...
+  float M = l;
+  #pragma unroll
+  for (int o = G; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float Ms = M == -INFINITY ? 0.f : M;
+  const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
+  float S2 = wl;
+  #pragma unroll
+  for (int o = G; o < 64; o <<= 1) S2 += __shfl_xor(S2, o);
+  float4_v acc[E / 4];
+  #pragma unroll
+  for (int k = 0; k < E / 4; ++k) acc[k] = float4_v{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+  for (int u = 0; u < 64 / G; ++u) {
+    const float wp = __shfl(wl, (u << LG) + hgd);
+    #pragma unroll
+    for (int k = 0; k < E / 4; ++k) acc[k] = u < nsrc ? acc[k] + wp * v[u][k] : acc[k];
+  }
+  const float Sd = __shfl(S2, hgd);
+  const float inv = Sd > 0.f ? 1.f / Sd : 0.f;
+  #pragma unroll
+  for (int k = 0; k < E / 4; ++k) {
+    const float4_v o = acc[k] * inv;
+    const int64_t off = base * D + e0 + 4 * k;
+    if constexpr (BF16) {
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    } else {
+      *reinterpret_cast<float4_v *>(static_cast<float *>(a.out) + off) = o;
+    }
+  }
+  if (lane < G && a.lse) a.lse[base + lane] = S2 > 0.f ? (Ms + log2_hw(S2)) * kLn2 : -INFINITY;
 }
 
 // The same merge for the G query heads of one kv head at once: one wave per (sequence, new token, kv
@@ -286,14 +400,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, PrefixArgs p
 // same sources, and their partial rows are G consecutive rows of every source: the wave finds the
 // sources once, reads the G x sources LSEs one per lane, and streams each source's G x D block with
 // E = G D / 64 consecutive floats per lane.  Rows that do not fit (sources x G > 64, or heads split
-// over two row tiles) take the per-row merge.
+// over two row tiles) take the per-row merge.  With piece slots on and uniform new tokens the sources
+// need no search: the item's piece count comes back with the sequence's length, and then only the
+// slots it names are read (with this many rows, reading every slot up front costs more than the wait).
 template <bool BF16, int D, int E>
 __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
   constexpr int G = E * 64 / D;             // heads per kv head, a power of two
   constexpr int LG = G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   static_assert((1 << LG) == G, "G must be 2, 4, 8 or 16");
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int H = a.num_heads;
   const int KVH = a.num_kv_heads;
   const int64_t nw = (int64_t)a.num_seqs * a.max_q_len * KVH;
@@ -302,6 +418,40 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
   const int64_t t = wid / KVH;
   const int i = (int)(t % a.max_q_len);
   const int s = (int)(t / a.max_q_len);
+  const int rpt = a.rows_per_tile;
+  const int rt = i * G / rpt;
+  const bool one_tile = rt == (i * G + G - 1) / rpt;
+  const int64_t stride = (int64_t)a.total_q * H;          // between partitions
+  // lane = j G + hg: source j's LSE for head hg; this lane's E floats of each source's G x D block:
+  // head hgd, dims d0 .. d0 + E - 1
+  const int j = lane >> LG;
+  const int hgl = lane & (G - 1);
+  const int e0 = lane * E;
+  float4_v v[64 / G][E / 4];
+  if (a.max_pieces > 1 && !a.q_lens && one_tile) {
+    const int row = s * a.max_q_len + i;
+    const int64_t base = (int64_t)row * H + kvh * G;
+    const int mp = a.max_pieces;
+    const int ctx_raw = a.context_lens[s];
+    const int cnt = a.item_cnt[((int64_t)s * KVH + kvh) * a.row_tiles + rt];
+    const float l0 = j < mp ? a.part_lse[j * stride + base + hgl] : -INFINITY;
+    int ctx = min(min(ctx_raw, a.max_context_len), a.max_blocks_per_seq * kBlock);
+    ctx = max(ctx, 0);
+    const int qs = max(1, min(a.max_q_len, ctx));
+    if (i >= qs || ctx <= 0 || row >= a.total_q) return;
+    if (cnt <= 1) return;                                 // one piece: the G rows are final already
+    if (cnt <= mp && cnt <= 64 / G) {
+      // many rows: the slots are read once the count is known, so no load is spent on unused ones
+      #pragma unroll
+      for (int u = 0; u < 64 / G; ++u) {
+        const float4_v *op = reinterpret_cast<const float4_v *>(a.part_o + ((int64_t)u * stride + base) * D + e0);
+        #pragma unroll
+        for (int k = 0; k < E / 4; ++k) v[u][k] = u < cnt ? op[k] : float4_v{0.f, 0.f, 0.f, 0.f};
+      }
+      group_merge<BF16, D, E>(a, base, lane, j < cnt ? l0 : -INFINITY, v, cnt);
+      return;
+    }
+  }
   const bool spill = a.spill_base >= 0;
   const int pre_s = spill ? a.item_pre[s] : 0;
   const int pre_all = spill ? a.item_pre[a.num_seqs] : 0;
@@ -309,11 +459,8 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
   if (i >= si.qs || si.ctx <= 0) return;
   const int row = si.qbase + i;
   if (row >= a.total_q) return;
-  const int64_t stride = (int64_t)a.total_q * H;          // between partitions
   const int64_t base = (int64_t)row * H + kvh * G;        // head kvh G + hg: row base + hg
-  const int rpt = a.rows_per_tile;
-  const int rt = i * G / rpt;
-  if (rt != (i * G + G - 1) / rpt) {                      // heads split over two row tiles
+  if (!one_tile) {                                        // heads split over two row tiles
     for (int hg = 0; hg < G; ++hg) combine_row<BF16, D, false>(a, PrefixArgs{}, s, i, kvh * G + hg, lane);
     return;
   }
@@ -356,7 +503,9 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
     const int64_t bn = share_raw(L, NW, ord + 1);
     const int obn = bn < pos1 ? real_off(bn) : nblk;
     if (obn <= ob) return false;
-    prow = a.spill_base + (int64_t)share_slot(W, ord) * rpt + srow;
+    // piece slots on (then there is one partition): pieces below max_pieces sit in partition rows
+    const int kp = a.max_pieces > 1 ? piece_index(L, NW, C, pos0, ord, a.max_pieces) : a.max_pieces;
+    prow = kp < a.max_pieces ? kp * stride + base : a.spill_base + (int64_t)share_slot(W, ord) * rpt + srow;
     return true;
   };
   const int nsrc = si.nparts + ncand;
@@ -373,10 +522,7 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
     return;
   }
 
-  // lane = j G + hg: source j's LSE for head hg.  A non-source points at partition 0's rows (always
-  // written) with weight 0.
-  const int j = lane >> LG;
-  const int hgl = lane & (G - 1);
+  // a non-source points at partition 0's rows (always written) with weight 0
   int64_t prow = base;
   bool cut = false;
   const bool ok = j < nsrc && source(j, prow, cut);
@@ -384,10 +530,6 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
   const float l = ok ? a.part_lse[prow + hgl] : -INFINITY;
   const int lo = (int)prow;
   const int hi = (int)(prow >> 32);
-  // this lane's E floats of each source's G x D block: head hgd, dims d0 .. d0 + E - 1
-  const int e0 = lane * E;
-  const int hgd = e0 / D;
-  float4_v v[64 / G][E / 4];
   #pragma unroll
   for (int u = 0; u < 64 / G; ++u) {
     const int src = u << LG;                              // the lane holding source u's row
@@ -396,39 +538,7 @@ __global__ __launch_bounds__(256) void combine_group_kernel(DecodeArgs a) {
     #pragma unroll
     for (int k = 0; k < E / 4; ++k) v[u][k] = op[k];
   }
-  // per-head max and weight sum over the sources: lanes hg, hg + G, hg + 2G, ...
-  float M = l;
-  #pragma unroll
-  for (int o = G; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float Ms = M == -INFINITY ? 0.f : M;
-  const float wl = l == -INFINITY ? 0.f : exp2_hw(l - Ms);
-  float S2 = wl;
-  #pragma unroll
-  for (int o = G; o < 64; o <<= 1) S2 += __shfl_xor(S2, o);
-  float4_v acc[E / 4];
-  #pragma unroll
-  for (int k = 0; k < E / 4; ++k) acc[k] = float4_v{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-  for (int u = 0; u < 64 / G; ++u) {
-    const float wp = u < nsrc ? __shfl(wl, (u << LG) + hgd) : 0.f;
-    #pragma unroll
-    for (int k = 0; k < E / 4; ++k) acc[k] += wp * v[u][k];
-  }
-  const float Sd = __shfl(S2, hgd);
-  const float inv = Sd > 0.f ? 1.f / Sd : 0.f;
-  #pragma unroll
-  for (int k = 0; k < E / 4; ++k) {
-    const float4_v o = acc[k] * inv;
-    const int64_t off = base * D + e0 + 4 * k;
-    if constexpr (BF16) {
-      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
-          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-    } else {
-      *reinterpret_cast<float4_v *>(static_cast<float *>(a.out) + off) = o;
-    }
-  }
-  if (lane < G && a.lse) a.lse[base + lane] = S2 > 0.f ? (Ms + log2_hw(S2)) * kLn2 : -INFINITY;
-
+  group_merge<BF16, D, E>(a, base, lane, l, v, nsrc);
 }
 
 // Exclusive prefix sum of q_lens into q_start[0..n]; one workgroup of 1024 threads.
@@ -475,9 +585,11 @@ hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, const Pr
   const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * a.num_heads;
   const int grid = (int)((waves + 3) / 4);
   const PrefixArgs none{};
+  // per-row merge: the first 16 or 32 piece slots in its first round trip (uniform new tokens only)
+  const int ns = a.max_pieces > 1 && !a.q_lens ? (a.max_pieces <= 16 ? 16 : 32) : 0;
   if (pre) {
-    if (head_dim == 64) combine_kernel<true, 64, true><<<grid, 256, 0, st>>>(a, *pre);
-    else combine_kernel<true, 128, true><<<grid, 256, 0, st>>>(a, *pre);
+    if (head_dim == 64) combine_kernel<true, 64, true, 0><<<grid, 256, 0, st>>>(a, *pre);
+    else combine_kernel<true, 128, true, 0><<<grid, 256, 0, st>>>(a, *pre);
   } else if (bf16 && group_e(a, head_dim) > 0) {
     const int gg = (int)(((int64_t)a.num_seqs * a.max_q_len * a.num_kv_heads + 3) / 4);
     switch (head_dim * 1000 + group_e(a, head_dim)) {
@@ -488,12 +600,24 @@ hipError_t launch_combine(const DecodeArgs &a, bool bf16, int head_dim, const Pr
       case 128008: combine_group_kernel<true, 128, 8><<<gg, 256, 0, st>>>(a); break;
       default: combine_group_kernel<true, 128, 16><<<gg, 256, 0, st>>>(a); break;
     }
-  } else if (bf16) {
-    if (head_dim == 64) combine_kernel<true, 64, false><<<grid, 256, 0, st>>>(a, none);
-    else combine_kernel<true, 128, false><<<grid, 256, 0, st>>>(a, none);
   } else {
-    if (head_dim == 64) combine_kernel<false, 64, false><<<grid, 256, 0, st>>>(a, none);
-    else combine_kernel<false, 128, false><<<grid, 256, 0, st>>>(a, none);
+    // bf16 / fp32 output x head dim x slots read up front
+    auto go = [&](auto kernel) { kernel<<<grid, 256, 0, st>>>(a, none); };
+    const int key = (bf16 ? 1000 : 0) + (head_dim == 64 ? 100 : 0) + ns;
+    switch (key) {
+      case 1100: go(combine_kernel<true, 64, false, 0>); break;
+      case 1116: go(combine_kernel<true, 64, false, 16>); break;
+      case 1132: go(combine_kernel<true, 64, false, 32>); break;
+      case 1000: go(combine_kernel<true, 128, false, 0>); break;
+      case 1016: go(combine_kernel<true, 128, false, 16>); break;
+      case 1032: go(combine_kernel<true, 128, false, 32>); break;
+      case 100: go(combine_kernel<false, 64, false, 0>); break;
+      case 116: go(combine_kernel<false, 64, false, 16>); break;
+      case 132: go(combine_kernel<false, 64, false, 32>); break;
+      case 16: go(combine_kernel<false, 128, false, 16>); break;
+      case 32: go(combine_kernel<false, 128, false, 32>); break;
+      default: go(combine_kernel<false, 128, false, 0>); break;
+    }
   }
   return hipGetLastError();
 }

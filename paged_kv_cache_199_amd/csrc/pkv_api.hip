@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "decode_args.h"
@@ -74,8 +75,10 @@ struct Plan {
   int item_cost;     // persistent schedule: pages of stream charged to each work item's start
   int64_t part_rows; // partial rows: num_parts * total_q * num_heads, plus the spill rows
   int64_t spill_base;
+  int max_pieces;    // persistent schedule without fixed partitions: piece slots per work item (else 0)
+  int64_t items;     // work items (sequences x kv heads x row tiles)
   bool need_q_start;
-  size_t off_q_start, off_item_pre, off_part_lse, off_part_o, bytes;
+  size_t off_q_start, off_item_pre, off_item_cnt, off_part_lse, off_part_o, bytes;
 };
 
 int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
@@ -189,6 +192,16 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
     pl.grid = cu_count() * per_cu / 8 * 8;
     if (pl.grid < 8) pl.grid = 8;
     pl.spill_base = (int64_t)pl.num_parts * total_q * num_heads;
+    if (pl.num_parts == 1) {
+      // piece slots: the first pieces of every work item go to partition rows, so the merge reads
+      // them with no search.  An item's pieces are about the waves per item, more for the longer
+      // items: twice that plus two covers the configured batches' longest items (more pieces go
+      // to spill rows and the general merge), at most 32.
+      pl.items = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
+      const int64_t per_item = ceil_div((int64_t)pl.grid * 4, pl.items > 0 ? pl.items : 1);
+      pl.max_pieces = (int)std::min<int64_t>(32, std::max<int64_t>(4, 2 * per_item + 2));
+      pl.spill_base = (int64_t)pl.max_pieces * total_q * num_heads;
+    }
     pl.part_rows = pl.spill_base + (int64_t)pl.grid * 4 * R;
   }
   pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
@@ -197,6 +210,8 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
   pl.off_item_pre = off;
   if (persist) off = align_up(off + (size_t)(num_seqs + 1) * 4);
+  pl.off_item_cnt = off;
+  if (pl.max_pieces > 1) off = align_up(off + (size_t)pl.items * 4);
   pl.off_part_lse = off;
   pl.off_part_o = off;
   if (pl.part_rows > 0) {
@@ -348,6 +363,8 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
   a.cut_align = pl.num_parts > 1 ? pl.depth : 1;
   a.item_cost = pl.item_cost;
   a.rows_per_tile = pl.rows_per_tile;
+  a.max_pieces = pl.max_pieces;
+  a.item_cnt = pl.max_pieces > 1 ? reinterpret_cast<int32_t *>(ws + pl.off_item_cnt) : nullptr;
   // the persistent matrix-core kernel appends in its own pass (up to 8 new tokens per sequence);
   // every other launch appends with a small kernel first
   const bool appending = new_k != nullptr;

@@ -20,6 +20,7 @@ oracle on every row, at the sizes and shapes where these rules decide the pieces
 """
 import random
 
+import numpy as np
 import pytest
 
 B = 16   # tokens per page
@@ -36,7 +37,33 @@ def first_share_above(L, NW, pos):
     return c
 
 
-def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_above):
+def first_share_above_f32(L, NW, pos):
+    """The decode kernel's form: ceil((pos + 1) NW / L) from a single-precision quotient, settled by
+    exact integer products (NW when no share starts above pos)."""
+    t = (pos + 1) * NW
+    if t >= L * NW:
+        return NW
+    c = min(max(int(np.float32(t) / np.float32(L)), 0), NW)
+    steps = 0
+    while c * L < t:
+        c += 1
+        steps += 1
+    down = 0
+    while c > 0 and (c - 1) * L >= t:
+        c -= 1
+        down += 1
+    return c, steps, down
+
+
+def piece_index(L, NW, cost, pos0, o, cap, first_above=first_share_above):
+    """Slot of the piece share o starts inside the item at stream pos0 (no fixed partitions)."""
+    if L < NW:
+        return cap
+    return min(o - first_above(L, NW, pos0 + cost) + 1, cap)
+
+
+def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_above, max_pieces=0,
+             piece=piece_index):
     S = len(ctxs)
     nblk = [(x + B - 1) // B for x in ctxs]
     qs = [max(1, min(q, x)) for q, x in zip(qls, ctxs)]
@@ -71,6 +98,8 @@ def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_a
         rr = ro - ro % N
         return b - off + (cost + rr if rr > 0 else 0)
 
+    slots = max_pieces > 1 and PP >= 10 ** 6   # piece slots exist only without fixed partitions
+    counts = {}   # (kvh, s, rt) -> the piece count the item-ending run stores
     pieces = []   # (kvh, s, rt, first page, end page, ord, destination)
     for o in range(NW):
         k, k_end = cut(share_raw(L, NW, o)), cut(share_raw(L, NW, o + 1))
@@ -89,6 +118,12 @@ def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_a
             if j0 > 0:
                 assert first, "only the share's first piece starts inside an item"
             nparts = (ctxs[s] + PP * B - 1) // (PP * B)
+            kp = 0
+            if slots:
+                if j0 > 0:
+                    kp = piece(L, NW, cost, kvh * I + pre[s] + t * span[s], o, max_pieces)
+                if j0 + run == nblk[s]:
+                    counts[(kvh, s, t)] = kp + 1 if kp < max_pieces else max_pieces + 1
             j = j0
             while j < j0 + run:   # pieces also end at partition ends
                 pend = min(j0 + run, (j // PP + 1) * PP)
@@ -96,6 +131,8 @@ def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_a
                     dest = ("final",)
                 elif j % PP == 0:
                     dest = ("part", j // PP)
+                elif slots and kp < max_pieces:
+                    dest = ("part", kp)
                 else:
                     dest = ("spill", o)
                 pieces.append((kvh, s, t, j, pend, o, dest))
@@ -145,13 +182,28 @@ def simulate(ctxs, qls, G, ROWS, KVH, cost, NW, N, PP, first_above=first_share_a
                     obn = real_off(bn) if bn < pos1 else nblk[s]
                     if obn <= ob:
                         continue
-                    sources.add(("spill", o))
-                written = {p[6] for p in pieces if p[:3] == (kvh, s, t)}
+                    kp = piece(L, NW, cost, pos0, o, max_pieces) if slots else max_pieces
+                    sources.add(("part", kp) if kp < max_pieces else ("spill", o))
+                mine = sorted((p for p in pieces if p[:3] == (kvh, s, t)), key=lambda p: p[3])
+                written = [p[6] for p in mine]
+                assert len(set(written)) == len(written), ("two pieces share a row", written)
+                written = set(written)
                 if nparts <= 1 and not any_cut:
                     assert written == {("final",)}, (written, kvh, s, t)
                 else:
                     assert ("final",) not in written
                     assert written == sources, (written, sources, kvh, s, t, cost, N, PP)
+                if slots:
+                    # the count the item-ending run stores, and the slots the one-round-trip merge
+                    # reads when it is at most max_pieces: pieces in stream order fill slots 0, 1, ...
+                    # (a stream shorter than the wave count has empty shares: pieces past the first
+                    # take spill rows and the count sends the merge to its search)
+                    nslot = max_pieces if L >= NW else 1
+                    cnt = counts[(kvh, s, t)]
+                    assert cnt == (len(mine) if len(mine) <= nslot else max_pieces + 1), (cnt, len(mine))
+                    for rank, p in enumerate(mine):
+                        if p[6] != ("final",):
+                            assert p[6] == (("part", rank) if rank < nslot else ("spill", p[5])), (rank, p)
     return pieces
 
 
@@ -176,6 +228,55 @@ def test_every_page_once_and_merge_sources_match_the_pieces(seed):
     rng = random.Random(seed)
     for _ in range(75):
         simulate(**random_shape(rng))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_piece_slots_follow_stream_order_and_the_count(seed):
+    # no fixed partitions, slots on: the first max_pieces pieces of an item (in stream order) take
+    # partition rows 0 .. max_pieces - 1, the rest their waves' spill rows, and the stored count says
+    # how many there are (max_pieces + 1 past that); small and large slot counts, streams shorter
+    # than the wave count included (their pieces all take spill rows)
+    rng = random.Random(100 + seed)
+    for _ in range(75):
+        shape = random_shape(rng)
+        shape.update(N=1, PP=10 ** 6)
+        simulate(**shape, max_pieces=rng.choice([4, 6, 18, 32]))
+
+
+def test_piece_index_catches_an_off_by_one():
+    # planted mistake: the slot formula counts one share too few
+    def short_by_one(L, NW, cost, pos0, o, cap):
+        return cap if L < NW else min(o - first_share_above(L, NW, pos0 + cost), cap)
+
+    rng = random.Random(12)
+    with pytest.raises(AssertionError):
+        for _ in range(50):
+            shape = random_shape(rng)
+            shape.update(N=1, PP=10 ** 6)
+            simulate(**shape, max_pieces=32, piece=short_by_one)
+
+
+def test_single_precision_share_search_is_exact():
+    # the kernel's share search against the exact one: stream lengths up to 2^31, up to 2^13 waves,
+    # positions at share boundaries and off them; the estimate is never above the answer and at most
+    # two below it
+    rng = random.Random(5)
+    for _ in range(20000):
+        L = rng.choice([rng.randint(1, 5000), rng.randint(1, 1 << 20), rng.randint(1 << 30, (1 << 31) - 1)])
+        NW = rng.choice([8, 64, 1024, 2048, 8192, 8 * rng.randint(1, 1024)])
+        if rng.random() < 0.5:
+            o = rng.randint(0, NW)
+            pos = max(share_raw(L, NW, o) + rng.choice([-1, 0, 1]), 0)
+        else:
+            pos = rng.randint(0, L + 2)
+        want = (-(-(pos + 1) * NW // L)) if (pos + 1) * NW < L * NW else NW
+        got = first_share_above_f32(L, NW, pos)
+        if isinstance(got, tuple):
+            got, up, down = got
+            assert up <= 2 and down == 0, (L, NW, pos, up, down)
+        assert got == want, (L, NW, pos, got, want)
+        if L <= 5000 and NW <= 2048:
+            assert got == first_share_above(L, NW, pos), (L, NW, pos)
 
 
 def test_one_long_sequence_is_cut_across_many_waves():

@@ -65,7 +65,7 @@ def test_noalloc_fp32_and_fixed_partitions(gpu_lib):
 
 def test_noalloc_refuses_a_plan_larger_than_its_scratch(gpu_lib):
     """16-key partitions over 256 sequences of up to 32768 tokens: 2048 partitions x 256 rows x 64 heads
-    of fp32 partials, far past 32 MiB; refused on the host, nothing enqueued, outputs untouched."""
+    of fp32 partials, far past 64 MiB; refused on the host, nothing enqueued, outputs untouched."""
     S, H, KVH, D = 256, 64, 8, 128
     need = _lib.decode_workspace_bytes(S, S, 1, 32768, H, KVH, D, _lib.PKV_BF16, 16, _lib.PATH_MFMA, 0,
                                        _lib.SCHEDULE_GRID)
