@@ -265,33 +265,37 @@ __global__ __launch_bounds__(256) void decode_mfma_persistent_kernel(DecodeArgs 
     if (reach) append_load<D, F8>(a, si, kvh, lane, ar);
     WaveRows<D, NT> w;
     load_rows<D, NT>(a, si, kvh, rt * ROWS, si.qs * G, col, grp, w);
-    // piece slots: the index of the run's piece in its item (0 at the item's start; only a share's
-    // first run starts inside an item), worked out while the q rows load; the run that ends the item
-    // stores its piece count now, as only the merge after this kernel reads it
-    int kp = 0;
-    if (a.max_pieces > 1) {
-      if (j0 > 0) {
-        const int64_t pos0 = (int64_t)kvh * I + __builtin_amdgcn_readfirstlane(pre[s]) + (int64_t)rt * span;
-        kp = __builtin_amdgcn_readfirstlane(piece_index(L, NW, C, pos0, ord, a.max_pieces));
-      }
-      if (j0 + run == nblk && lane == 0)
-        a.item_cnt[((int64_t)s * a.num_kv_heads + kvh) * a.row_tiles + rt] = kp < a.max_pieces ? kp + 1 : a.max_pieces + 1;
-    }
     WaveAcc<D, NT> st;
     init_acc<D, NT>(st);
+    int kp = 0;
     stream_pages<D, NT, NBUF, F8>(
         a, si, kvh, bt_row, j0, j0 + run, PP, lane, w, st,
         [&](int part, int first, int end) {
           const bool whole = first == 0 && end == nblk && si.nparts == 1;
-          // with piece slots there is one partition, so a piece that starts inside it is the run's
-          if (first % PP == 0) finish_wave<D, NT>(a, part, whole, lane, w, st, -1);
-          else if (kp < a.max_pieces) finish_wave<D, NT>(a, kp, false, lane, w, st, -1);
-          else finish_wave<D, NT>(a, part, false, lane, w, st, spill_row0);
+          // a piece that starts a partition writes its row; with piece slots there is one partition,
+          // so a piece that starts inside it is the run's, and takes slot kp while there is one
+          const bool at_part = first % PP == 0;
+          const bool slot = !at_part && kp < a.max_pieces;
+          finish_wave<D, NT>(a, slot ? kp : part, whole, lane, w, st, at_part || slot ? -1 : spill_row0);
           init_acc<D, NT>(st);
         },
         [&](int j, uint4 *kr, uint2 *vr) {
           if constexpr (APPEND) {
             if (reach) append_patch<D, F8>(j, lane, ar, app_lds[wave], kr, vr);
+          }
+        },
+        [&] {
+          // piece slots, worked out while the first pages load: the index of the run's piece in its
+          // item (0 at the item's start; only a share's first run starts inside an item); the run
+          // that ends the item stores its piece count, which only the merge after this kernel reads
+          if (a.max_pieces > 1) {
+            if (j0 > 0) {
+              const int64_t pos0 = (int64_t)kvh * I + __builtin_amdgcn_readfirstlane(pre[s]) + (int64_t)rt * span;
+              kp = __builtin_amdgcn_readfirstlane(piece_index(L, NW, C, pos0, ord, a.max_pieces));
+            }
+            if (j0 + run == nblk && lane == 0)
+              a.item_cnt[((int64_t)s * a.num_kv_heads + kvh) * a.row_tiles + rt] =
+                  kp < a.max_pieces ? kp + 1 : a.max_pieces + 1;
           }
         });
     if (reach && rt == 0) append_store<D, F8>(a, kvh, bt_row, j0, j0 + run, lane, ar);

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void prefix_attend_f8_kernel(DecodeArgs a, Pre
   stream_pages<D, NT, NBUF, true>(
       ap, prefix_seq(pg), kvh, bt_row, jb, je, 1 << 30, lane, w, st,
       [&](int, int, int) { finish_wave<D, NT>(ap, 0, false, lane, w, st, item * kPrefixRows); },
-      [&](int, uint4 *, uint2 *) {});
+      [&](int, uint4 *, uint2 *) {}, [] {});
 }
 
 hipError_t launch_prefix_attend(const DecodeArgs &a, const PrefixArgs &p, int head_dim, bool f8, hipStream_t st) {

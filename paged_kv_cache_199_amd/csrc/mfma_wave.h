@@ -299,11 +299,12 @@ __device__ __forceinline__ void widen_page(const uint2 *kin, const uint4 *vin, u
 
 // F8: the pools hold E4M3 codes (1 byte per element) instead of bf16; pages are half as large and are
 // widened in registers right before their products.
-template <int D, int NT, int NBUF, bool F8, class Flush, class Patch>
+// start() runs once the first pages' loads are out, for work that can wait on them.
+template <int D, int NT, int NBUF, bool F8, class Flush, class Patch, class Start>
 __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
                                              const int32_t *bt_row, int jb, int je, int PP, int lane,
                                              const WaveRows<D, NT> &w, WaveAcc<D, NT> &st,
-                                             Flush flush, Patch patch) {
+                                             Flush flush, Patch patch, Start start) {
   constexpr int EB = F8 ? 1 : 2;          // bytes per cache element
   constexpr int ROWB = D * EB;
   constexpr int NK = D / 32;
@@ -358,6 +359,7 @@ __device__ __forceinline__ void stream_pages(const DecodeArgs &a, const SeqInfo 
   for (int j = 0; j < NBUF - 1; ++j) issue(id_of(jb + j), kb[j], vb[j], okb[j]);
   #pragma unroll
   for (int b = 0; b < NBUF; ++b) sid[b] = id_of(jb + NBUF - 1 + b);
+  start();
   int j0 = 0;
   int piece = jb;
   for (; j0 + NBUF <= n; j0 += NBUF) {
