@@ -253,6 +253,57 @@ def test_ragged_q_lens(gpu_lib):
         _check_all(w, P)
 
 
+def _stream_pages(w, plan):
+    """Pages of the balanced schedule's stream (virtual pages included), as the decode kernel lays it out."""
+    G = w.spec.num_heads // w.spec.num_kv_heads
+    R, C = plan["rows_per_tile"], plan["item_cost"]
+    nblk = (w.context_lens.astype(np.int64) + 15) // 16
+    rts = -(-w.q_lens.astype(np.int64) * G // R)
+    return int(((nblk + C) * rts * (nblk > 0)).sum()) * w.spec.num_kv_heads
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+def test_ragged_q_lens_over_piece_slots(gpu_lib, grouped):
+    """Ragged new tokens without fixed partitions, on a stream longer than the wave count. A row's
+    position then depends on the other sequences' q_lens, so the merge cannot take its one-round-trip
+    slot path. It searches instead, and must find each cut item's first pieces in partition (slot)
+    rows and any further ones in spill rows. Under 4096 rows this is the per-row merge; at 4096 or
+    more, the grouped one."""
+    rng = np.random.default_rng(31 + grouped)
+    if grouped:
+        S, H, KVH, D = 160, 32, 8, 64
+        ctx = rng.integers(64, 1200, S)
+        ql = np.minimum(rng.integers(1, 4, S), ctx)
+    else:
+        S, H, KVH, D = 12, 32, 8, 128
+        ctx = rng.integers(700, 6000, S)
+        ql = rng.integers(1, 6, S)
+    spec = W.custom(f"ragged_slots_{int(grouped)}", ctx.tolist(), q_len=ql.tolist(), num_heads=H,
+                    num_kv_heads=KVH, head_dim=D)
+    w = W.build(spec, DEV)
+    assert not w.uniform_q and (w.total_q * H >= 4096) == grouped
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, H, KVH, D, _lib.PKV_BF16,
+                            path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT)
+    assert plan["schedule"] == _lib.SCHEDULE_PERSISTENT and plan["num_partitions"] == 1
+    assert _stream_pages(w, plan) >= 4 * plan["grid_waves"]   # every share holds pages: slots in use
+    _check_persistent(w, 0, 2)
+
+
+def test_piece_slots_with_two_row_tiles(gpu_lib):
+    """Uniform new tokens (5 per sequence, GQA 8: 40 rows per kv head, two 32-row tiles), under 4096
+    rows and a stream of many pages per wave: the per-row merge reads each item's piece count and
+    slots in one round trip, with the item found from (sequence, token, head) through the row tile."""
+    rng = np.random.default_rng(41)
+    ctx = rng.integers(800, 6000, 10)
+    spec = W.custom("slots_two_tiles", ctx.tolist(), q_len=5, num_heads=64, num_kv_heads=8, head_dim=128)
+    w = W.build(spec, DEV)
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, 64, 8, 128, _lib.PKV_BF16,
+                            path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT)
+    assert w.uniform_q and w.total_q * 64 < 4096 and plan["row_tiles"] == 2 and plan["num_partitions"] == 1
+    assert _stream_pages(w, plan) >= 4 * plan["grid_waves"]
+    _check_persistent(w, 0, 2)
+
+
 def test_gqa8_and_mha(gpu_lib):
     for H, KVH in ((64, 8), (8, 8), (16, 1)):
         spec = W.custom(f"heads_{H}_{KVH}", [100, 700, 1500], num_heads=H, num_kv_heads=KVH, head_dim=128)
