@@ -68,6 +68,9 @@ EXPORTS = {
                                         _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int,
                                         ctypes.POINTER(DecodeOptions), _vp]),
     "pkv_copy_blocks": (_c_int, [_vp, _vp, _vp, _vp, ctypes.c_int32, _c_i64, _c_int, _c_int, _c_int, _vp]),
+    # device-side check of the decode preconditions (include/pkv_check.h)
+    "pkv_check_decode_inputs": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                         _vp, _vp]),
     # host-side block management (include/pkv_blocks.h); handles are opaque pointers
     "pkv_block_pool_create": (_vp, [ctypes.c_int32]),
     "pkv_block_pool_destroy": (None, [_vp]),
@@ -406,6 +409,41 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, q_lens, 
                                     max_context_len, NB, num_heads, num_kv_heads, head_dim, block_size,
                                     float(scale), code, ctypes.byref(o), _stream(stream))
     _check(rc, "pkv_paged_attn_prefill")
+
+
+# pkv_check_reason (include/pkv_check.h)
+CHECK_REASONS = {0: "ok", 1: "q_len", 2: "q_over_context", 3: "context_len", 4: "context_table", 5: "block_id",
+                 6: "q_total"}
+CHECK_REPORT_INTS = 8
+
+
+def check_decode_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor, q_lens: Optional[torch.Tensor],
+                        num_blocks: int, total_q: int, max_q_len: int, max_context_len: int, block_size: int = 16,
+                        stream=None) -> dict:
+    """Check a decode batch's device-side preconditions on the GPU (pkv_check_decode_inputs) and return
+    the report: violations, the first bad sequence (-1: none), its reason (a CHECK_REASONS name) and
+    offending value, and the q_lens sum.  Synchronizes `stream` to read the report: a debugging aid,
+    not a step of the decode."""
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.is_contiguous()
+          and block_tables.shape[1] >= 1, "block_tables: int32 [S, max_blocks >= 1], contiguous")
+    S = block_tables.shape[0]
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == S and context_lens.is_contiguous(),
+          "context_lens: int32 [S]")
+    if q_lens is not None:
+        _need(q_lens.dtype == torch.int32 and q_lens.numel() == S and q_lens.is_contiguous(), "q_lens: int32 [S]")
+    _on_gpu_like(block_tables, "check arguments", context_lens, q_lens)
+    with torch.cuda.device(block_tables.device):
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            report = torch.empty(CHECK_REPORT_INTS, dtype=torch.int32, device=block_tables.device)
+        _check(load().pkv_check_decode_inputs(_ptr(block_tables), _ptr(context_lens), _ptr(q_lens), S,
+                                              int(block_tables.shape[1]), int(total_q), int(max_q_len),
+                                              int(max_context_len), int(num_blocks), int(block_size), _ptr(report),
+                                              ctypes.c_void_p(s.cuda_stream)), "pkv_check_decode_inputs")
+        s.synchronize()
+    r = report.cpu().tolist()
+    return {"violations": r[0], "first_seq": r[1], "reason": CHECK_REASONS.get(r[2], r[2]), "value": r[3],
+            "q_sum": r[4]}
 
 
 def shared_prefix_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,

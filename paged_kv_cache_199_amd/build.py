@@ -16,7 +16,8 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pkv_api.hip", "kv_cache_write.hip", "decode_valu.hip", "decode_mfma.hip",
-           "decode_combine.hip", "block_manager.hip", "decode_prefix.hip", "prefill_mfma.hip"]
+           "decode_combine.hip", "block_manager.hip", "decode_prefix.hip", "prefill_mfma.hip",
+           "check_inputs.hip"]
 # the benchmark's page-stream probe (include/pkv_probe.h) is a library of its own, not part of libpkv.so
 PROBE_SOURCES = ["stream_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")

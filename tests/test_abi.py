@@ -191,6 +191,31 @@ def test_prefill_argument_validation(lib):
     assert call(S=0, q=None) == 0
 
 
+def test_check_argument_validation(lib):
+    f = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+
+    def call(bt=f, ctx=f, rep=f, S=4, mb=8, mq=1, nb=64, B=16):
+        return lib.pkv_check_decode_inputs(bt, ctx, None, S, mb, S, mq, 128, nb, B, rep, None)
+    assert call(rep=None) == -1 and call(rep=None, S=0) == -1
+    assert call(bt=None) == -1 and call(ctx=None) == -1
+    assert call(B=32) == -3
+    assert call(S=-1) == -2 and call(mb=0) == -2 and call(mq=0) == -2 and call(nb=-1) == -2
+
+
+def test_check_binding_rejects_bad_tables_without_gpu():
+    import torch
+
+    bt = torch.zeros((4, 0), dtype=torch.int32)
+    with pytest.raises(ValueError):                  # a table with no entries holds no context
+        _lib.check_decode_inputs(bt, torch.ones(4, dtype=torch.int32), None, 8, 4, 1, 16)
+    with pytest.raises(ValueError):                  # int64 tables
+        _lib.check_decode_inputs(torch.zeros((4, 2), dtype=torch.int64), torch.ones(4, dtype=torch.int32), None,
+                                 8, 4, 1, 16)
+    with pytest.raises(ValueError):                  # host tensors: their pointers must never reach a kernel
+        _lib.check_decode_inputs(torch.zeros((4, 2), dtype=torch.int32), torch.ones(4, dtype=torch.int32), None,
+                                 8, 4, 1, 16)
+
+
 @pytest.fixture(scope="module")
 def probe():
     if not os.path.exists(PROBE_LIB):
