@@ -17,12 +17,12 @@ constexpr int kCheckBlock = 16;
 // The first precondition sequence s breaks (pkv_check_reason) and its offending value; lengths and
 // the table row as the caller passed them.  Every lane of the wave calls it: lanes split the table
 // row, and the result is wave-uniform.
-struct Verdict {
+struct Finding {
   int reason;
   int value;
 };
 
-__device__ Verdict check_seq(const int32_t *bt, const int32_t *ctx_lens, const int32_t *q_lens, int s,
+__device__ Finding check_seq(const int32_t *bt, const int32_t *ctx_lens, const int32_t *q_lens, int s,
                              int max_blocks_per_seq, int max_q_len, int max_context_len, int64_t num_blocks,
                              int lane) {
   const int ctx = ctx_lens[s];
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void check_scan_kernel(const int32_t *bt, cons
   const int lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (s >= num_seqs) return;
-  const Verdict v = check_seq(bt, ctx_lens, q_lens, s, max_blocks_per_seq, max_q_len, max_context_len, num_blocks,
+  const Finding v = check_seq(bt, ctx_lens, q_lens, s, max_blocks_per_seq, max_q_len, max_context_len, num_blocks,
                               lane);
   if (lane == 0) {
     atomic_add(report + 4, q_lens ? q_lens[s] : max_q_len);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64) void check_final_kernel(const int32_t *bt, cons
   int bad = report[0];
   int reason = PKV_CHECK_OK, value = 0;
   if (first != INT_MAX) {
-    const Verdict v = check_seq(bt, ctx_lens, q_lens, first, max_blocks_per_seq, max_q_len, max_context_len,
+    const Finding v = check_seq(bt, ctx_lens, q_lens, first, max_blocks_per_seq, max_q_len, max_context_len,
                                 num_blocks, lane);
     reason = v.reason;
     value = v.value;
