@@ -146,8 +146,15 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   // stays within 0.2% up to 4 and loses 0.3-0.5% at 6-8.
   pl.item_cost = pl.schedule == PKV_SCHEDULE_PERSISTENT ? 4 : 0;
   const bool persist = pl.schedule == PKV_SCHEDULE_PERSISTENT;
+  // small batches over E4M3 pools: at most 64 pages per wave at one workgroup per CU, bounded from
+  // max_context_len.  A page there carries the decode's arithmetic for half the bytes, and a deeper
+  // ring keeps more of them in flight per wave (below).
+  const int64_t pages_bound =
+      (int64_t)num_seqs * num_kv_heads * pl.row_tiles * ceil_div(max_context_len, kBlockSize);
+  const bool small_f8 = persist && dtype == PKV_BF16_FP8KV && pages_bound <= 64LL * 4 * cu_count();
   pl.depth = (opts && opts->pipeline_depth) ? opts->pipeline_depth
-                                            : pkv::mfma_default_depth(head_dim, R, persist);
+             : small_f8                       ? 4
+                                              : pkv::mfma_default_depth(head_dim, R, persist);
   int P = opts ? opts->partition_size : 0;
   const int whole = ceil_div(max_context_len, kBlockSize) * kBlockSize;
   if (persist) {
@@ -178,17 +185,15 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   if (persist) {
     // every wave of the grid owns rows_per_tile spill rows after the partition rows
     // one workgroup per CU unless asked: fewer, longer shares measured faster than a full CU of
-    // waves (less per-wave start-up and fewer cut pieces to merge) on all five workloads.  Over E4M3
-    // pools a page carries the same arithmetic for half the bytes, and small batches (at most 64
-    // pages per wave at one workgroup per CU, bounded from max_context_len) run two per CU: conc32
-    // over E4M3 pools 32.8 -> 31.9 us; long context over E4M3 pools was 0.8% slower at two.
+    // waves (less per-wave start-up and fewer cut pieces to merge) on all five workloads.  Small
+    // batches over E4M3 pools ran two per CU at ring depth 2 (conc32 over E4M3 pools 32.8 -> 31.9
+    // us) until the merge read piece slots; since then one per CU at depth 4 is faster there:
+    // 26.5 -> 26.1 us in three interleaved repetitions (the decode 0.6 us slower, the merge over
+    // 10 slots instead of 18 more than that faster).  Long context over E4M3 pools was 0.8% slower
+    // at two.
     const int fits = pkv::mfma_persistent_wgs_per_cu(head_dim, R, pl.depth, num_seqs);
     const int asked_wgs = opts ? opts->workgroups_per_cu : 0;
-    const int64_t pages_bound =
-        (int64_t)num_seqs * num_kv_heads * pl.row_tiles * ceil_div(max_context_len, kBlockSize);
-    const bool small_f8 = dtype == PKV_BF16_FP8KV && pages_bound <= 64LL * 4 * cu_count();
-    const int want = small_f8 ? 2 : 1;
-    const int per_cu = asked_wgs > 0 ? (asked_wgs < fits ? asked_wgs : fits) : (want < fits ? want : fits);
+    const int per_cu = asked_wgs > 0 ? (asked_wgs < fits ? asked_wgs : fits) : 1;
     pl.grid = cu_count() * per_cu / 8 * 8;
     if (pl.grid < 8) pl.grid = 8;
     pl.spill_base = (int64_t)pl.num_parts * total_q * num_heads;
