@@ -1,0 +1,79 @@
+"""GPU parity on seeded random batch shapes: head dims, GQA groups, batch sizes, length mixes (short,
+long, page-boundary, one long among short), uniform and ragged new tokens, bf16 and E4M3 pools, each
+through a kernel family and schedule drawn at random (balanced persistent split with piece slots,
+persistent with fixed partitions, and for bf16 pools the grid schedule and the VALU path), compared
+with the oracle on every row.
+The shapes are drawn, not chosen: they reach combinations the targeted tests do not list."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_199_amd import _lib
+from paged_kv_cache_199_amd import workloads as W
+from tests.gpu_helpers import BF16_TOL, LSE_TOL, compare, oracle_full, run_library
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+B = 16
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def draw(seed):
+    rng = np.random.default_rng(5000 + seed)
+    D = int(rng.choice([64, 128]))
+    KVH = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.choice([1, 3, 8, 17, 40, 100]))
+    mix = rng.choice(["short", "long", "edges", "one_long", "wide"])
+    if mix == "short":
+        ctx = rng.integers(1, 200, S)
+    elif mix == "long":
+        ctx = rng.integers(1000, 4000 if S <= 17 else 1500, S)
+    elif mix == "edges":
+        ctx = rng.choice([1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 1023, 1024, 1025], S)
+    elif mix == "one_long":
+        ctx = rng.integers(8, 120, S)
+        ctx[rng.integers(0, S)] = 6000 if S <= 17 else 3000
+    else:
+        ctx = rng.integers(1, 2500 if S <= 40 else 800, S)
+    f8 = bool(rng.random() < 0.3)
+    qmax = int(rng.choice([1, 1, 2, 5]))
+    ragged = bool(rng.random() < 0.5) and qmax > 1
+    ql = np.minimum(rng.integers(1, qmax + 1, S) if ragged else np.full(S, qmax), ctx)
+    if not ragged and (ql != qmax).any():       # uniform new tokens need every context to hold them
+        ctx = np.maximum(ctx, qmax)
+        ql = np.full(S, qmax)
+    variant = rng.choice(["persist", "persist", "persist_parts", "grid", "valu"])
+    if f8 and variant in ("valu", "grid"):       # E4M3 pools decode with the persistent schedule only
+        variant = "persist"
+    depth = int(rng.choice([2, 3, 4]))
+    return dict(D=D, KVH=KVH, H=KVH * G, ctx=ctx.astype(int).tolist(), ql=ql.astype(int).tolist(), f8=f8,
+                variant=str(variant), depth=depth, mix=str(mix))
+
+
+VARIANTS = {
+    "persist": lambda d: dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT, depth=d, partition_size=0),
+    "persist_parts": lambda d: dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT, depth=d,
+                                    partition_size=256),
+    "grid": lambda d: dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_GRID, depth=d, partition_size=0),
+    "valu": lambda d: dict(path=_lib.PATH_VALU, schedule=_lib.SCHEDULE_AUTO, depth=0, partition_size=0),
+}
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_shape(gpu_lib, seed):
+    c = draw(seed)
+    spec = W.custom(f"rand{seed}", c["ctx"], q_len=c["ql"], num_heads=c["H"], num_kv_heads=c["KVH"],
+                    head_dim=c["D"], seed=100 + seed, kv_fp8=c["f8"])
+    w = W.build(spec, DEV)
+    kw = VARIANTS[c["variant"]](c["depth"])
+    _say(f"[case] seed {seed}: S={w.num_seqs} H={c['H']} KVH={c['KVH']} D={c['D']} mix={c['mix']} "
+         f"q<={w.max_q_len} {'ragged' if not w.uniform_q else 'uniform'} {'E4M3' if c['f8'] else 'bf16'} "
+         f"{c['variant']} {kw}")
+    out, lse = run_library(w, DEV, **kw)
+    d_out, d_lse = compare(w, out, lse, *oracle_full(w))
+    _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+    assert np.isfinite(d_out) and d_out <= BF16_TOL
+    assert np.isfinite(d_lse) and d_lse <= LSE_TOL
