@@ -1,9 +1,12 @@
-"""GPU parity on seeded random batch shapes: head dims, GQA groups, batch sizes, length mixes (short,
+"""GPU parity on seeded random batch shapes, for decode and for prefill.
+
+Decode: head dims, GQA groups, batch sizes, length mixes (short,
 long, page-boundary, one long among short), uniform and ragged new tokens, bf16 and E4M3 pools, each
 through a kernel family and schedule drawn at random (balanced persistent split with piece slots,
 persistent with fixed partitions, and for bf16 pools the grid schedule and the VALU path), compared
-with the oracle on every row.
-The shapes are drawn, not chosen: they reach combinations the targeted tests do not list."""
+with the oracle on every row.  Prefill: whole prompts and chunks over cached contexts, uniform and
+ragged, bf16 and E4M3 pools, over poisoned pools.  The shapes are drawn, not chosen: they reach
+combinations the targeted tests do not list."""
 import numpy as np
 import pytest
 
@@ -73,6 +76,61 @@ def test_random_shape(gpu_lib, seed):
          f"q<={w.max_q_len} {'ragged' if not w.uniform_q else 'uniform'} {'E4M3' if c['f8'] else 'bf16'} "
          f"{c['variant']} {kw}")
     out, lse = run_library(w, DEV, **kw)
+    d_out, d_lse = compare(w, out, lse, *oracle_full(w))
+    _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+    assert np.isfinite(d_out) and d_out <= BF16_TOL
+    assert np.isfinite(d_lse) and d_lse <= LSE_TOL
+
+
+def draw_prefill(seed):
+    rng = np.random.default_rng(7000 + seed)
+    D = int(rng.choice([64, 128]))
+    KVH = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.choice([1, 2, 5, 9]))
+    prompt = bool(rng.random() < 0.4)
+    uniform = bool(rng.random() < 0.3)
+    if prompt:
+        q = np.full(S, int(rng.integers(1, 700))) if uniform else rng.integers(1, 700, S)
+        ctx = q.copy()
+    else:
+        q = np.full(S, int(rng.integers(1, 600))) if uniform else rng.integers(1, 600, S)
+        ctx = q + rng.integers(0, 3000, S)
+    # keep the oracle's work (new tokens x context x heads) to a few seconds
+    while int((q * ctx).sum()) * KVH * G > 4e7 and S > 1:
+        S -= 1
+        q, ctx = q[:S], ctx[:S]
+    while int((q * ctx).sum()) * KVH * G > 4e7:
+        q = np.maximum(q // 2, 1)
+        ctx = np.maximum(ctx // 2, q)
+    return dict(D=D, KVH=KVH, H=KVH * G, ctx=ctx.astype(int).tolist(), ql=q.astype(int).tolist(),
+                f8=bool(rng.random() < 0.3), prompt=prompt, uniform=uniform)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_prefill_shape(gpu_lib, seed):
+    """Prefill and chunked prefill on seeded random shapes over poisoned pools (every slot no sequence
+    may read holds NaN), bf16 and E4M3."""
+    import torch
+
+    from tests.gpu_helpers import nan_empty, nan_like
+
+    c = draw_prefill(seed)
+    spec = W.custom(f"rand_prefill{seed}", c["ctx"], q_len=c["ql"], num_heads=c["H"], num_kv_heads=c["KVH"],
+                    head_dim=c["D"], seed=300 + seed, kv_fp8=c["f8"])
+    w = W.build(spec, DEV, poison=True)
+    _say(f"[case] prefill seed {seed}: S={w.num_seqs} H={c['H']} KVH={c['KVH']} D={c['D']} "
+         f"{'prompt' if c['prompt'] else 'chunk'} q<={w.max_q_len} ctx<={w.max_context_len} "
+         f"{'uniform' if w.uniform_q else 'ragged'} {'E4M3' if c['f8'] else 'bf16'}")
+    meta = w.device_meta(DEV)
+    out = nan_like(w.q)
+    lse = nan_empty((w.total_q, w.spec.num_heads), DEV)
+    scales = dict(k_scale=w.spec.k_scale, v_scale=w.spec.v_scale) if w.kv_fp8 else {}
+    _lib.paged_attn_prefill(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"],
+                            None if w.uniform_q else meta["q_lens"], out, lse, w.spec.num_heads,
+                            w.spec.num_kv_heads, w.spec.head_dim, 16, w.scale, w.max_context_len, w.max_q_len,
+                            **scales)
+    torch.cuda.synchronize()
     d_out, d_lse = compare(w, out, lse, *oracle_full(w))
     _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
     assert np.isfinite(d_out) and d_out <= BF16_TOL
