@@ -1,4 +1,4 @@
-"""GPU parity on seeded random batch shapes, for decode and for prefill.
+"""GPU parity on seeded random batch shapes, for decode, prefill and the decode step with its append.
 
 Decode: head dims, GQA groups, batch sizes, length mixes (short,
 long, page-boundary, one long among short), uniform and ragged new tokens, bf16 and E4M3 pools, each
@@ -135,3 +135,30 @@ def test_random_prefill_shape(gpu_lib, seed):
     _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
     assert np.isfinite(d_out) and d_out <= BF16_TOL
     assert np.isfinite(d_lse) and d_lse <= LSE_TOL
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_append_shape(gpu_lib, seed):
+    """The decode step with its append on seeded random bf16 shapes (1..9 new tokens, so also past the
+    fused limit of 8), through a drawn schedule: caches equal the oracle's scatter bit for bit, outputs
+    match the oracle, and the one call equals write-then-decode bit for bit."""
+    from tests.test_gpu_append import _check as check_append
+
+    rng = np.random.default_rng(9000 + seed)
+    S = int(rng.choice([1, 4, 13, 32]))
+    KVH = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    q = int(rng.choice([1, 2, 5, 9]))
+    ragged = bool(rng.random() < 0.5) and q > 1
+    ctx = rng.integers(q, 1500, S)
+    ql = rng.integers(1, q + 1, S) if ragged else np.full(S, q)
+    spec = W.custom(f"rand_append{seed}", ctx.astype(int).tolist(), q_len=ql.astype(int).tolist(),
+                    num_heads=KVH * G, num_kv_heads=KVH, head_dim=D, seed=500 + seed)
+    variant = [dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT, depth=int(rng.choice([2, 3, 4]))),
+               dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_PERSISTENT, partition_size=128),
+               dict(path=_lib.PATH_MFMA, schedule=_lib.SCHEDULE_GRID),
+               dict(path=_lib.PATH_VALU)][int(rng.integers(0, 4))]
+    _say(f"[case] append seed {seed}: S={S} H={KVH * G} KVH={KVH} D={D} q<={q} "
+         f"{'ragged' if ragged else 'uniform'} {variant}")
+    check_append(W.build(spec, DEV), [variant])
