@@ -1,4 +1,5 @@
-"""GPU parity on seeded random batch shapes, for decode, prefill and the decode step with its append.
+"""GPU parity on seeded random batch shapes: decode, prefill, the decode step with its append, and the
+read-once shared-prefix decode.
 
 Decode: head dims, GQA groups, batch sizes, length mixes (short,
 long, page-boundary, one long among short), uniform and ragged new tokens, bf16 and E4M3 pools, each
@@ -162,3 +163,35 @@ def test_random_append_shape(gpu_lib, seed):
     _say(f"[case] append seed {seed}: S={S} H={KVH * G} KVH={KVH} D={D} q<={q} "
          f"{'ragged' if ragged else 'uniform'} {variant}")
     check_append(W.build(spec, DEV), [variant])
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_read_once_shape(gpu_lib, seed):
+    """Read-once shared-prefix decode on seeded random batches: one to four groups of consecutive
+    sequences sharing drawn prefixes (members shorter than the prefix share what they have), ungrouped
+    sequences before and after them, uniform or ragged new tokens, bf16 or E4M3 pools, forced
+    read-once; against the oracle and the plain decode."""
+    from tests.test_gpu_prefix import _check as check_prefix
+
+    rng = np.random.default_rng(11000 + seed)
+    S = int(rng.choice([3, 8, 20, 48]))
+    KVH = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    f8 = bool(rng.random() < 0.3)
+    q = int(rng.choice([1, 1, 3]))
+    ragged = bool(rng.random() < 0.5) and q > 1
+    ctx = rng.integers(q, 2500, S)
+    ql = rng.integers(1, q + 1, S) if ragged else np.full(S, q)
+    spec = W.custom(f"rand_prefix{seed}", ctx.astype(int).tolist(), q_len=ql.astype(int).tolist(),
+                    num_heads=KVH * G, num_kv_heads=KVH, head_dim=D, seed=700 + seed, kv_fp8=f8)
+    w = W.build(spec, DEV)
+    # groups are consecutive runs of sequences; the ones before the first and after the last share nothing
+    lo = int(rng.integers(0, S // 3 + 1))
+    hi = int(rng.integers(max(lo + 1, 2 * S // 3), S + 1))
+    n = min(hi - lo, int(rng.integers(1, 5)))
+    edges = [lo] + np.sort(rng.choice(np.arange(lo + 1, hi), size=n - 1, replace=False)).tolist() + [hi]
+    groups = [(a, b, 16 * int(rng.integers(1, 80))) for a, b in zip(edges[:-1], edges[1:])]
+    _say(f"[case] read-once seed {seed}: S={S} H={KVH * G} KVH={KVH} D={D} q<={q} "
+         f"{'ragged' if ragged else 'uniform'} {'E4M3' if f8 else 'bf16'} groups {groups}")
+    check_prefix(w, W.share_prefixes(w, groups), f"read-once seed {seed}")
