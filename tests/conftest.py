@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The built library on a GPU.  Fails loudly (not skips) when the library is missing on a GPU machine."""
+    """The built library on a GPU.  Fails loudly (not skips) when the library is missing on a machine with a GPU."""
     import torch
 
     if not torch.cuda.is_available():
