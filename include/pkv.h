@@ -145,11 +145,14 @@ int pkv_kv_cache_write_fp8(const void *k, const void *v, const int64_t *slot_map
  * step, with temporary device memory taken from bounded, reused pools; here the caller owns that
  * memory and this call says how much one decode call needs, so a serving loop sizes it once and
  * reuses it for every step.
- * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options (0 is possible:
- * a single-partition grid launch with uniform q needs none).  The split-K partials take
- * ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes; the persistent
- * schedule adds (num_seqs + 1) * 4 bytes and rows_per_tile * (head_dim + 1) * 4 bytes per wave of
- * its grid (the value depends on the device's CU count).
+ * Bytes of device workspace pkv_paged_attn_decode needs for these sizes and options with its full
+ * plan (0 is possible: a single-partition grid launch with uniform q needs none).  The split-K
+ * partials take ceil(max_context_len / P) * total_q * num_heads * (head_dim + 1) * 4 bytes; the
+ * persistent schedule adds (num_seqs + 1) * 4 bytes and rows_per_tile * (head_dim + 1) * 4 bytes per
+ * wave of its grid, and without fixed partitions it keeps piece slots: the first pieces its split
+ * cuts from each work item get total_q * num_heads * (head_dim + 1) * 4 bytes each, up to 32 slots
+ * (plan_info.piece_slots), plus 4 bytes per work item.  The value depends on the device's CU count.
+ * A smaller workspace of at least plan_info.min_workspace_bytes also serves (fewer slots, below).
  */
 size_t pkv_decode_workspace_bytes(int num_seqs, int total_q, int max_q_len, int max_context_len,
                                   int num_heads, int num_kv_heads, int head_dim, int dtype,
@@ -169,6 +172,12 @@ typedef struct pkv_decode_plan_info {
   int item_cost;           /* persistent schedule: stream pages charged to each (sequence, kv head,
                               row tile) work item's start when the page stream is cut into equal
                               shares; else 0 */
+  int piece_slots;         /* persistent schedule without fixed partitions: pieces of each work item
+                              whose partials sit at fixed rows (the merge reads them with no search);
+                              0 = none (every piece past the first in spill rows) */
+  size_t min_workspace_bytes;  /* the smallest workspace the call accepts: the plan with no piece
+                                  slots (equal to workspace_bytes when the plan has none); added in
+                                  ABI 1.1 */
 } pkv_decode_plan_info;
 
 /* Fills *info; returns PKV_OK or a negative pkv_status on bad sizes / options. */
@@ -183,8 +192,11 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
  * Preconditions on device data: 1 <= q_lens[s] <= context_lens[s] <= max_context_len,
  * context_lens[s] <= max_blocks_per_seq * block_size, block ids in [0, num_blocks), and
  * sum(q_lens) == total_q (q_lens == NULL: total_q == num_seqs * max_q_len).
- * `workspace` must hold pkv_decode_workspace_bytes() bytes (may be NULL when that is 0); its contents
- * on entry do not matter.
+ * `workspace` holds pkv_decode_workspace_bytes() bytes for the full plan (may be NULL when that is 0);
+ * its contents on entry do not matter.  A workspace_bytes below that but at least
+ * plan_info.min_workspace_bytes runs the same kernels with as many piece slots as fit (the results
+ * agree within rounding: the merge sums the same partials, found by a search instead of at fixed
+ * rows); below the minimum the call returns PKV_ERR_WORKSPACE.
  * `scale` multiplies the raw dot products (usually 1/sqrt(head_dim)).
  */
 int pkv_paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -228,12 +240,15 @@ int pkv_paged_attn_decode_append(const void *q, const void *new_k, const void *n
  * forbid hipMalloc): pkv_paged_attn_decode without a workspace argument.  The split-K partials, spill
  * rows and tables the decode keeps in its workspace go to a static device array of the library
  * instead, PKV_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on, held until the process
- * ends.  Nothing is allocated: no hipMalloc / hipFree and no allocating library routine.  A call whose
- * plan needs more scratch than that (pkv_decode_workspace_bytes() larger; e.g. fixed partitions over
- * very long batches) returns PKV_ERR_SCRATCH and enqueues nothing.  Every call on one GPU shares that
- * GPU's array, so calls that overlap on one GPU (different streams, or host threads) race: serialize
+ * ends.  Nothing is allocated: no hipMalloc / hipFree and no allocating library routine.  The call
+ * is pkv_paged_attn_decode with a workspace of PKV_NOALLOC_SCRATCH_BYTES bytes: the full plan when it
+ * fits (then the results are the same bits as with a workspace of pkv_decode_workspace_bytes()),
+ * else the plan with as many piece slots as fit; a call whose plan needs more scratch than that
+ * even without slots (plan_info.min_workspace_bytes larger; e.g. fixed partitions over very long
+ * batches) returns PKV_ERR_SCRATCH and enqueues nothing.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (different streams, or host threads) race: serialize
  * them.  The decode needs nothing in the scratch to start at zero.  Arguments, preconditions, results
- * and the other errors are those of pkv_paged_attn_decode; the results are the same bits.
+ * and the other errors are those of pkv_paged_attn_decode with that workspace, bit for bit.
  */
 #define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int pkv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,

@@ -35,7 +35,7 @@ class DecodePlanInfo(ctypes.Structure):
     _fields_ = [("partition_size", _c_int), ("num_partitions", _c_int), ("path", _c_int),
                 ("rows_per_tile", _c_int), ("row_tiles", _c_int), ("pipeline_depth", _c_int),
                 ("schedule", _c_int), ("grid_waves", _c_int), ("workspace_bytes", _c_sz),
-                ("item_cost", _c_int)]
+                ("item_cost", _c_int), ("piece_slots", _c_int), ("min_workspace_bytes", _c_sz)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -297,8 +297,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
 
     q_lens None means every sequence has max_q_len new tokens.  max_context_len is a host-known upper
     bound of context_lens (the kernels never read device data on the host).  A workspace tensor
-    (any dtype, contiguous, on the GPU) of at least decode_workspace_bytes() bytes is allocated when
-    not given.  `events` = (begin, end) torch.cuda.Event pair that has been recorded once: the library
+    (any dtype, contiguous, on the GPU) of decode_workspace_bytes() bytes is allocated when not given;
+    a given one may be smaller, down to decode_plan()["min_workspace_bytes"] (fewer piece slots).  `events` = (begin, end) torch.cuda.Event pair that has been recorded once: the library
     records them around its partition kernel."""
     lib = load()
     total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
@@ -343,7 +343,8 @@ def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: t
                               wgs_per_cu: int = 0, k_scale: float = 0.0, v_scale: float = 0.0) -> None:
     """paged_attn_decode for callers that cannot allocate (pkv_paged_attn_decode_noalloc): the library's
     static per-GPU scratch (NOALLOC_SCRATCH_BYTES) replaces the workspace, and nothing is allocated here
-    or in the library.  Calls that overlap on one GPU share that scratch and race."""
+    or in the library.  The same bits as paged_attn_decode with a workspace of that size (fewer piece
+    slots when the full plan needs more).  Calls that overlap on one GPU share that scratch and race."""
     lib = load()
     total_q, S, NB, code = _check_decode_args(q, k_cache, v_cache, block_tables, context_lens, q_lens, out, lse,
                                               num_heads, num_kv_heads, head_dim, block_size)

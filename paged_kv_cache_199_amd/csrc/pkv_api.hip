@@ -116,7 +116,7 @@ int shape_status(int num_seqs, int total_q, int max_q_len, int max_context_len, 
 // half the maximum.  No split at all when the whole context fits one partition.
 Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, int num_heads,
                int num_kv_heads, int head_dim, int dtype, bool ragged_q,
-               const pkv_decode_options *opts) {
+               const pkv_decode_options *opts, size_t budget = SIZE_MAX) {
   Plan pl{};
   const bool bf16 = dtype != PKV_F32;
   const int G = num_heads / num_kv_heads;
@@ -183,7 +183,6 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
   pl.spill_base = -1;
   pl.part_rows = pl.num_parts > 1 ? (int64_t)pl.num_parts * total_q * num_heads : 0;
   if (persist) {
-    // every wave of the grid owns rows_per_tile spill rows after the partition rows
     // one workgroup per CU unless asked: fewer, longer shares measured faster than a full CU of
     // waves (less per-wave start-up and fewer cut pieces to merge) on all five workloads.  Small
     // batches over E4M3 pools ran two per CU at ring depth 2 (conc32 over E4M3 pools 32.8 -> 31.9
@@ -196,35 +195,48 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
     const int per_cu = asked_wgs > 0 ? (asked_wgs < fits ? asked_wgs : fits) : 1;
     pl.grid = cu_count() * per_cu / 8 * 8;
     if (pl.grid < 8) pl.grid = 8;
-    pl.spill_base = (int64_t)pl.num_parts * total_q * num_heads;
     if (pl.num_parts == 1) {
       // piece slots: the first pieces of every work item go to partition rows, so the merge reads
       // them with no search.  An item's pieces are about the waves per item, more for the longer
       // items: twice that plus two covers the configured batches' longest items (more pieces go
-      // to spill rows and the general merge), at most 32.
+      // to spill rows and the general merge), at most 32; fewer when the workspace is short (below).
       pl.items = (int64_t)num_seqs * num_kv_heads * pl.row_tiles;
       const int64_t per_item = ceil_div((int64_t)pl.grid * 4, pl.items > 0 ? pl.items : 1);
       pl.max_pieces = (int)std::min<int64_t>(32, std::max<int64_t>(4, 2 * per_item + 2));
-      pl.spill_base = (int64_t)pl.max_pieces * total_q * num_heads;
     }
-    pl.part_rows = pl.spill_base + (int64_t)pl.grid * 4 * R;
   }
   pl.need_q_start = ragged_q;   // the combine kernel reads q_start too
-  size_t off = 0;
-  pl.off_q_start = off;
-  if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
-  pl.off_item_pre = off;
-  if (persist) off = align_up(off + (size_t)(num_seqs + 1) * 4);
-  pl.off_item_cnt = off;
-  if (pl.max_pieces > 1) off = align_up(off + (size_t)pl.items * 4);
-  pl.off_part_lse = off;
-  pl.off_part_o = off;
-  if (pl.part_rows > 0) {
-    off = align_up(off + (size_t)pl.part_rows * 4);
+  // rows of partials and the workspace layout for pl.max_pieces piece slots; under the persistent
+  // schedule every wave of the grid owns rows_per_tile spill rows after the partition rows
+  auto lay_out = [&] {
+    if (persist) {
+      const int64_t first_rows = pl.max_pieces > 1 ? pl.max_pieces : pl.num_parts;
+      pl.spill_base = first_rows * total_q * num_heads;
+      pl.part_rows = pl.spill_base + (int64_t)pl.grid * 4 * R;
+    }
+    size_t off = 0;
+    pl.off_q_start = off;
+    if (ragged_q) off = align_up(off + (size_t)(num_seqs + 1) * 4);
+    pl.off_item_pre = off;
+    if (persist) off = align_up(off + (size_t)(num_seqs + 1) * 4);
+    pl.off_item_cnt = off;
+    if (pl.max_pieces > 1) off = align_up(off + (size_t)pl.items * 4);
+    pl.off_part_lse = off;
     pl.off_part_o = off;
-    off = align_up(off + (size_t)pl.part_rows * head_dim * 4);
+    if (pl.part_rows > 0) {
+      off = align_up(off + (size_t)pl.part_rows * 4);
+      pl.off_part_o = off;
+      off = align_up(off + (size_t)pl.part_rows * head_dim * 4);
+    }
+    pl.bytes = off;
+  };
+  lay_out();
+  // a workspace too small for this plan: fewer piece slots, down to none (the pieces past the slots
+  // go to spill rows, which the merge finds by its search); each slot costs total_q * num_heads rows
+  while (pl.bytes > budget && pl.max_pieces > 1) {
+    pl.max_pieces = pl.max_pieces > 2 ? pl.max_pieces - 1 : 0;
+    lay_out();
   }
-  pl.bytes = off;
   return pl;
 }
 
@@ -232,7 +244,7 @@ Plan make_plan(int num_seqs, int total_q, int max_q_len, int max_context_len, in
 
 extern "C" {
 
-int pkv_version(void) { return (1 << 16) | 0; }
+int pkv_version(void) { return (1 << 16) | 1; }
 
 const char *pkv_status_string(int status) {
   switch (status) {
@@ -310,6 +322,10 @@ int pkv_decode_plan(int num_seqs, int total_q, int max_q_len, int max_context_le
   info->schedule = pl.schedule;
   info->workspace_bytes = pl.bytes;
   info->item_cost = pl.item_cost;
+  info->piece_slots = pl.max_pieces;
+  info->min_workspace_bytes = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
+                                        head_dim, dtype, true, opts, 0)
+                                  .bytes;
   return PKV_OK;
 }
 
@@ -337,8 +353,9 @@ int decode_impl(const void *q, const void *new_k, const void *new_v, const void 
 
   const bool bf16 = dtype != PKV_F32;       // the dtype of q and out
   const bool f8 = dtype == PKV_BF16_FP8KV;
+  // a workspace short of the full plan's bytes gets the plan with as many piece slots as it holds
   const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads,
-                            head_dim, dtype, q_lens != nullptr, opts);
+                            head_dim, dtype, q_lens != nullptr, opts, workspace ? workspace_bytes : 0);
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes)) return PKV_ERR_WORKSPACE;
   const int64_t units = (int64_t)num_kv_heads * pl.num_parts * num_seqs * pl.row_tiles;
   if (units + 8 >= kMaxGrid || (int64_t)num_seqs * max_q_len * num_heads / 4 + 1 >= kMaxGrid)
@@ -491,8 +508,9 @@ int pkv_paged_attn_decode_noalloc(const void *q, const void *k_cache, const void
                               head_dim, dtype, opts);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
+  // the plan decode_impl makes for a workspace of the scratch's size
   const Plan pl = make_plan(num_seqs, total_q, max_q_len, max_context_len, num_heads, num_kv_heads, head_dim,
-                            dtype, q_lens != nullptr, opts);
+                            dtype, q_lens != nullptr, opts, PKV_NOALLOC_SCRATCH_BYTES);
   if (pl.bytes > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
   void *ws = scratch_on_current_device();
   if (!ws) return PKV_ERR_SCRATCH;

@@ -121,6 +121,28 @@ def test_workspace_and_partition_policy(lib):
     assert info.rows_per_tile == 32 and info.row_tiles == 1
 
 
+def test_piece_slots_and_the_smallest_workspace(lib):
+    """The persistent plan without fixed partitions keeps piece slots, each total_q * num_heads rows of
+    head_dim + 1 floats, plus one count per work item; the smallest workspace it accepts is the plan
+    with none.  The grid schedule and fixed partitions keep no slots."""
+    info = _lib.DecodePlanInfo()
+    S, H, KVH, D = 512, 64, 8, 128
+    assert lib.pkv_decode_plan(S, S, 1, 200, H, KVH, D, 1, None, ctypes.byref(info)) == 0
+    # 4096 work items over the grid's waves: an item is cut about once, so the floor of 4 slots
+    assert info.schedule == _lib.SCHEDULE_PERSISTENT and info.piece_slots == 4
+    row_set = S * H * (D + 1) * 4
+    extra = info.workspace_bytes - info.min_workspace_bytes
+    assert 0 <= extra - ((info.piece_slots - 1) * row_set + S * KVH * 4) < 3 * 256
+    assert info.workspace_bytes > (64 << 20) > info.min_workspace_bytes   # the no-alloc scratch needs fewer
+    # few, long items: more pieces per item, more slots (at most 32)
+    assert lib.pkv_decode_plan(6, 6, 1, 6000, 8, 2, D, 1, None, ctypes.byref(info)) == 0
+    assert info.piece_slots == 32
+    for opts in (_lib.DecodeOptions(0, 0, 0, _lib.SCHEDULE_GRID, None, None),
+                 _lib.DecodeOptions(256, 0, 0, 0, None, None)):
+        assert lib.pkv_decode_plan(S, S, 1, 2000, H, KVH, D, 1, ctypes.byref(opts), ctypes.byref(info)) == 0
+        assert info.piece_slots == 0 and info.min_workspace_bytes == info.workspace_bytes
+
+
 def test_append_argument_validation(lib):
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
 

@@ -1,0 +1,89 @@
+"""GPU: a decode workspace short of the full plan's bytes runs the plan with fewer piece slots, down to
+none (include/pkv.h: at least the plan info's min_workspace_bytes).  At each size the output matches
+the oracle and the full plan's output; one byte below the minimum is refused before anything runs.
+The workspaces are poisoned (NaN in every word) so that a slot the merge reads but no piece wrote
+would show."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_199_amd import _lib
+from paged_kv_cache_199_amd import workloads as W
+from tests.gpu_helpers import BF16_TOL, LSE_TOL, compare, nan_empty, nan_like, oracle_all, poisoned_workspace
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _code(w):
+    return _lib.PKV_BF16_FP8KV if w.kv_fp8 else _lib.PKV_BF16
+
+
+def _run(w, nbytes):
+    meta = w.device_meta(DEV)
+    out = nan_like(w.q)
+    lse = nan_empty((w.total_q, w.spec.num_heads), DEV)
+    scales = dict(k_scale=w.spec.k_scale, v_scale=w.spec.v_scale) if w.kv_fp8 else {}
+    _lib.paged_attn_decode(w.q, w.k_cache, w.v_cache, meta["block_tables"], meta["context_lens"],
+                           None if w.uniform_q else meta["q_lens"], out, lse, w.spec.num_heads, w.spec.num_kv_heads,
+                           w.spec.head_dim, 16, w.scale, w.max_context_len, max_q_len=w.max_q_len,
+                           workspace=poisoned_workspace(nbytes, DEV), **scales)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _widen(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+CASES = {
+    # few long items cut into many pieces: 32 slots, the rest in spill rows; per-row merge of slots
+    "one_long_uniform": lambda: W.custom("ws_one_long", [1, 17, 300, 6000, 513, 2000], q_len=1, num_heads=8,
+                                         num_kv_heads=2, head_dim=128, seed=41),
+    # ragged new tokens: the general merge, slots or spill rows by piece index
+    "one_long_ragged": lambda: W.custom("ws_one_long_ragged", [1, 17, 300, 6000, 513, 2000], q_len=[1, 2, 5, 1, 3, 2],
+                                        num_heads=8, num_kv_heads=2, head_dim=128, seed=42),
+    # E4M3 pools, a conc-32-like batch: about 10 slots
+    "e4m3_32": lambda: W.custom("ws_e4m3", np.random.default_rng(43).integers(500, 4000, 32).tolist(), q_len=1,
+                                num_heads=32, num_kv_heads=8, head_dim=128, seed=43, kv_fp8=True),
+    # 16384 rows: the merge by kv-head group (one wave per group of 8 heads)
+    "grouped_512": lambda: W.custom("ws_grouped", np.random.default_rng(44).integers(1, 400, 512).tolist(), q_len=1,
+                                    num_heads=32, num_kv_heads=4, head_dim=64, seed=44),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_fewer_piece_slots_for_a_short_workspace(gpu_lib, case):
+    w = W.build(CASES[case](), DEV)
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, w.spec.num_heads,
+                            w.spec.num_kv_heads, w.spec.head_dim, _code(w))
+    full, least, slots = plan["workspace_bytes"], plan["min_workspace_bytes"], plan["piece_slots"]
+    assert plan["schedule"] == _lib.SCHEDULE_PERSISTENT and slots >= 4 and least < full
+    if w.uniform_q:
+        # the plan query sizes for ragged new tokens, whose q_start table (num_seqs + 1 ints, in a
+        # 256-byte aligned region) a call without q_lens does not keep
+        q_start = -(-(w.num_seqs + 1) * 4 // 256) * 256
+        full, least = full - q_start, least - q_start
+    ref_out, ref_lse, ref_vabs = oracle_all(w)
+    base = None
+    for nbytes, what in ((full, f"full plan ({slots} slots)"), (full - 1, "one byte short (one slot fewer)"),
+                         ((full + least) // 2, "halfway"), (least, "the minimum (no slots)")):
+        _say(f"[case] {case}: workspace {nbytes} B, {what}")
+        out, lse = _run(w, nbytes)
+        d_out, d_lse = compare(w, out, lse, ref_out, ref_lse, ref_vabs)
+        _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+        assert np.isfinite(d_out) and d_out <= BF16_TOL
+        assert np.isfinite(d_lse) and d_lse <= LSE_TOL
+        if base is None:
+            base = (_widen(out), _widen(lse))
+        else:
+            # the same partials merged from other rows: rounding apart, the full plan's result
+            assert np.max(np.abs(_widen(out) - base[0])) <= 2.0 ** -7 * max(1.0, float(np.max(np.abs(base[0]))))
+            assert np.max(np.abs(_widen(lse) - base[1])) <= 1e-5
+    _say(f"[case] {case}: workspace {least - 1} B, below the minimum")
+    with pytest.raises(RuntimeError, match="workspace"):
+        _run(w, least - 1)

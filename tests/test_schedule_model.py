@@ -234,13 +234,14 @@ def test_every_page_once_and_merge_sources_match_the_pieces(seed):
 def test_piece_slots_follow_stream_order_and_the_count(seed):
     # no fixed partitions, slots on: the first max_pieces pieces of an item (in stream order) take
     # partition rows 0 .. max_pieces - 1, the rest their waves' spill rows, and the stored count says
-    # how many there are (max_pieces + 1 past that); small and large slot counts, streams shorter
-    # than the wave count included (their pieces all take spill rows)
+    # how many there are (max_pieces + 1 past that); small and large slot counts (down to the 2 a
+    # short workspace may leave), streams shorter than the wave count included (their pieces all take
+    # spill rows)
     rng = random.Random(100 + seed)
     for _ in range(75):
         shape = random_shape(rng)
         shape.update(N=1, PP=10 ** 6)
-        simulate(**shape, max_pieces=rng.choice([4, 6, 18, 32]))
+        simulate(**shape, max_pieces=rng.choice([2, 3, 4, 6, 18, 32]))
 
 
 def test_piece_index_catches_an_off_by_one():
