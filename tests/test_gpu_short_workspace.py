@@ -87,3 +87,29 @@ def test_fewer_piece_slots_for_a_short_workspace(gpu_lib, case):
     _say(f"[case] {case}: workspace {least - 1} B, below the minimum")
     with pytest.raises(RuntimeError, match="workspace"):
         _run(w, least - 1)
+
+
+def test_fused_append_with_the_smallest_workspace(gpu_lib):
+    """The decode step with its append (concurrency-32 batch, one new token each) on the smallest
+    workspace: the caches equal the oracle's scatter bit for bit and the outputs match the oracle."""
+    from oracle import paged_attention as O
+    from tests.gpu_helpers import host_bits, oracle_with_vabs
+    from tests.test_gpu_append import _decode, _new_rows, _slots
+
+    w = W.build(1, DEV)
+    plan = _lib.decode_plan(w.num_seqs, w.total_q, w.max_q_len, w.max_context_len, w.spec.num_heads,
+                            w.spec.num_kv_heads, w.spec.head_dim, _code(w))
+    assert w.uniform_q and plan["piece_slots"] >= 4
+    least = plan["min_workspace_bytes"] - -(-(w.num_seqs + 1) * 4 // 256) * 256
+    nk, nv = _new_rows(w)
+    want_k, want_v = O.kv_cache_write(host_bits(w.k_cache), host_bits(w.v_cache), host_bits(nk), host_bits(nv),
+                                      _slots(w))
+    ref = oracle_with_vabs(host_bits(w.q), want_k, want_v, w.block_tables, w.context_lens, w.q_lens, w.scale,
+                           w.spec.num_kv_heads, 16)
+    _say(f"[case] fused append on {w.spec.name}, workspace {least} B (no piece slots)")
+    kc, vc = w.k_cache.clone(), w.v_cache.clone()
+    out, lse = _decode(w, kc, vc, new=(nk, nv), workspace=poisoned_workspace(least, DEV))
+    assert np.array_equal(host_bits(kc), want_k) and np.array_equal(host_bits(vc), want_v)
+    d_out, d_lse = compare(w, out, lse, *ref)
+    _say(f"   max|d out| = {d_out:.3e}   max|d lse| = {d_lse:.3e}")
+    assert d_out <= BF16_TOL and d_lse <= LSE_TOL
