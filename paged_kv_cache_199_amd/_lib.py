@@ -460,8 +460,8 @@ def shared_prefix_workspace_bytes(num_seqs, total_q, max_q_len, max_context_len,
 class DecodeStep:
     """One decode step bound once: the optional append of the new tokens' K/V (through slot_mapping
     with pkv_kv_cache_write, or, given new_k / new_v without slot_mapping, in the decode call itself
-    with pkv_paged_attn_decode_append), then paged decode attention, with the same checks as kv_cache_write / paged_attn_decode done at
-    construction.  A call only enqueues the two C calls on the current stream, so a serving loop
+    with pkv_paged_attn_decode_append), then paged decode attention, with the same checks as
+    kv_cache_write / paged_attn_decode done at construction.  A call only enqueues the two C calls on the current stream, so a serving loop
     pays little host time per step and the step can be captured in a HIP graph.  A call may swap in
     other cache tensors of the same shape, dtype and device (not checked again)."""
 
