@@ -141,6 +141,166 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
   }
 }
 
+// ---- Value products at the full matrix-core rate (two 16-row tiles per wave, D = 128) ----
+// A 16-token page gives the P.V product only 16 keys, so v_mfma_f32_16x16x16_bf16 runs it at half
+// the matrix cores' rate (16 of the page step's 24 matrix-core instructions).  v_mfma_f32_32x32x16_bf16
+// takes the same 16 keys at the full rate: O^T[d][r] += sum_t V^T[d][t] P^T[t][r] for 32 dims x 32
+// rows, four instructions per page at D = 128 instead of sixteen.  Its operands (lane l: column
+// l % 32, keys 8 (l / 32) .. + 7; accumulator: column l % 32, rows 8 q + 4 (l / 32) + e in register
+// 4 q + e) take the V^T rows straight from LDS (16 bytes: 8 tokens of one dim) and the
+// probabilities from the score tiles with one lane swap per word: lane (c, g) of the 16x16 score
+// layout holds keys 4 g .. 4 g + 3 of row c of each tile, and v_permlane16_swap exchanges the odd
+// 16-lane rows of one register with the even rows of another, which puts tile 0's keys 0..7 and
+// 8..15 of row c on lanes c and c + 32 and tile 1's on lanes c + 16 and c + 48.
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct WaveAccWide {
+  static constexpr int NB = D / 32;
+  float m[2];            // running max per score tile (log2 units), equal on the 4 lanes of a column
+  float lsum[2];         // this lane's share of each tile's exp-sum
+  float16_t acc[NB];     // O^T for dims 32 b .. 32 b + 31: lane l holds row l % 32 (tile (l / 16) % 2)
+};
+
+template <int D>
+__device__ __forceinline__ void init_acc(WaveAccWide<D> &s) {
+  #pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    s.m[n] = kNegBig;
+    s.lsum[n] = 0.f;
+  }
+  #pragma unroll
+  for (int b = 0; b < WaveAccWide<D>::NB; ++b)
+    #pragma unroll
+    for (int e = 0; e < 16; ++e) s.acc[b][e] = 0.f;
+}
+
+// One 16-token page: the scores, mask and online softmax of mfma_page, then the value product at the
+// full rate.  vr[b]: this lane's V^T operand for dims 32 b + l % 32, tokens 8 (l / 32) .. + 7.
+template <int D>
+__device__ __forceinline__ void mfma_page_wide(const DecodeArgs &a, const SeqInfo &si, int bstart,
+                                               const uint4 *kr, uint4 *vr, bool ok, int lane,
+                                               const WaveRows<D, 2> &w, WaveAccWide<D> &st) {
+  constexpr int NK = D / 32;
+  constexpr int NB = D / 32;
+  const int grp = lane >> 4;
+  float4_t c[2], x[2];
+  #pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    float4_t c4 = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int k = 0; k < NK; ++k)
+      c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[k]), w.qB[n][k], c4, 0, 0, 0);
+    c[n] = c4;
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) x[n][e] = fmaf(c4[e], a.scale_log2, -st.m[n]);
+  }
+  if (!ok || bstart + kBlock > w.first_last + 1) {
+    const int pos0 = bstart + 4 * grp;
+    #pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      #pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!ok || pos0 + e > w.last[n]) x[n][e] = -INFINITY;
+    }
+    const int valid = ok ? si.ctx - bstart : 0;
+    if (valid < kBlock) {
+      // slots past the context may hold anything (even NaN): zero them so p = 0 adds exactly 0
+      const int k0 = 8 * (lane >> 5);
+      #pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        uint32_t wd[4] = {vr[b].x, vr[b].y, vr[b].z, vr[b].w};
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k0 + 2 * q >= valid) wd[q] = 0u;
+          else if (k0 + 2 * q + 1 >= valid) wd[q] &= 0xffffu;
+        }
+        vr[b] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    }
+  }
+  static_assert(kRescaleSlack >= 0.f, "the integer comparison needs a non-negative threshold");
+  int xbits = __float_as_int(x[0][0]);
+  #pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) xbits = max(xbits, __float_as_int(x[n][e]));
+  }
+  const bool need = xbits > __float_as_int(kRescaleSlack);
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    float alpha[2];
+    #pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      float4_t sc;
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = x[n][e] == -INFINITY ? -INFINITY : c[n][e] * a.scale_log2;
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(st.m[n], bm);
+      alpha[n] = exp2_hw(st.m[n] - mn);
+      st.m[n] = mn;
+      st.lsum[n] *= alpha[n];
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) x[n][e] = sc[e] - mn;
+    }
+    // lane l's accumulator rows are row l % 32 of tile (l / 16) % 2, the same column it holds there
+    const float al = (lane & 16) ? alpha[1] : alpha[0];
+    #pragma unroll
+    for (int b = 0; b < NB; ++b) st.acc[b] *= al;
+  }
+  uint32_t pw[2][2];
+  #pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const float p0 = exp2_hw(x[n][0]);
+    const float p1 = exp2_hw(x[n][1]);
+    const float p2 = exp2_hw(x[n][2]);
+    const float p3 = exp2_hw(x[n][3]);
+    st.lsum[n] += (p0 + p1) + (p2 + p3);
+    pw[n][0] = pack_bf16x2(p0, p1);
+    pw[n][1] = pack_bf16x2(p2, p3);
+  }
+  // even 16-lane rows: own tile-0 keys, then the next row's; odd rows: the previous row's tile-1
+  // keys, then their own
+  const auto s0 = __builtin_amdgcn_permlane16_swap(pw[0][0], pw[1][0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(pw[0][1], pw[1][1], false, false);
+  const bf16x8_t pB = __builtin_bit_cast(bf16x8_t, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+  #pragma unroll
+  for (int b = 0; b < NB; ++b)
+    st.acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vr[b]), pB, st.acc[b], 0, 0, 0);
+}
+
+// The final output (bf16) and natural-log LSE of the wave's rows from the wide accumulator.
+template <int D>
+__device__ __forceinline__ void finish_wave_wide(const DecodeArgs &a, int lane, const WaveRows<D, 2> &w,
+                                                 const WaveAccWide<D> &st) {
+  float l[2];
+  #pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    l[n] = st.lsum[n];
+    l[n] += __shfl_xor(l[n], 16);
+    l[n] += __shfl_xor(l[n], 32);
+  }
+  const int t = (lane >> 4) & 1;
+  const float lt = t ? l[1] : l[0];
+  if ((t ? w.last[1] : w.last[0]) < 0) return;
+  const bool seen = lt > 0.f;
+  const float inv = seen ? a.v_scale / lt : 0.f;
+  const float lse2 = seen ? (t ? st.m[1] : st.m[0]) + log2_hw(lt) : -INFINITY;
+  const int64_t orow = t ? w.orow[1] : w.orow[0];
+  uint16_t *o = static_cast<uint16_t *>(a.out) + orow * D + 4 * (lane >> 5);
+  #pragma unroll
+  for (int b = 0; b < WaveAccWide<D>::NB; ++b) {
+    #pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v0 = st.acc[b][4 * q] * inv, v1 = st.acc[b][4 * q + 1] * inv;
+      const float v2 = st.acc[b][4 * q + 2] * inv, v3 = st.acc[b][4 * q + 3] * inv;
+      *reinterpret_cast<uint2 *>(o + 32 * b + 8 * q) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+    }
+  }
+  if (lane < 32 && a.lse) a.lse[orow] = lse2 * kLn2;
+}
+
 // bf16 pools, D = 128: the same page walk with each stage fetched by gfx950's global-to-LDS loads
 // (global_load_lds_dwordx4), so no VGPRs hold pages in flight.  Such a load writes 16 bytes per lane
 // to consecutive LDS addresses (lane l at base + 16 l); each lane picks the global 16-byte chunk
@@ -160,11 +320,13 @@ struct DmaPages {
   static constexpr int BYTES = SP * PBYTES;          // one stage buffer
 };
 
-template <int NT, int SP>
+// WIDE: the value products at the full rate (mfma_page_wide; st a WaveAccWide, NT = 2), with V rows
+// swizzled by bit 3 of the dim so a 16-byte read of 16 consecutive dims hits 16 different bank groups.
+template <int NT, int SP, bool WIDE = false, class ST>
 __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const SeqInfo &si, int kvh,
                                                      const int32_t *bt, int jb, int je, int jw,
                                                      char *buf0, char *buf1, const WaveRows<128, NT> &w,
-                                                     WaveAcc<128, NT> &st) {
+                                                     ST &st) {
   typedef DmaPages<SP> L;
   constexpr int D = 128;
   constexpr int NK = D / 32;
@@ -186,7 +348,7 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const int k_slot_g = ((lane >> 2) - wave) & 3;
   const int k_off = (4 * wave + (lane & 3)) * (D * 2) + (4 * (lane >> 4) + k_slot_g) * 16;
   const int vd = 32 * wave + (lane >> 1);
-  const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> 2) & 1)) * 16);
+  const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> (WIDE ? 3 : 2)) & 1)) * 16);
   // block ids of the next stage to fetch (lane p: page p), read one stage ahead and issued after a
   // stage's global-to-LDS loads, so the stage-end wait covers both and no fetch waits for an id (read
   // when needed, the id's wait would also count the loads in flight)
@@ -224,17 +386,28 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
     const int gl = ln >> 4;
     const int kb = (cl >> 2) * 1024 + ((((cl >> 2) + gl) & 3) * 4 + (cl & 3)) * 16;
     const int vb = cl * (kBlock * 2) + ((gl >> 1) ^ ((cl >> 2) & 1)) * 16 + (gl & 1) * 8;
+    // WIDE: dim l % 32 of each 32-dim block, tokens 8 (l / 32) .. + 7
+    const int vw = (ln & 31) * (kBlock * 2) + (((ln >> 5) ^ ((ln >> 3) & 1)) * 16);
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
       if (j0 + p < jw) {
         const char *pg = src + p * L::PBYTES;
         uint4 kr[NK];
-        uint2 vr[ND];
         #pragma unroll
         for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(pg + kb + c * 256);
-        #pragma unroll
-        for (int t = 0; t < ND; ++t) vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + vb + t * 16 * (kBlock * 2));
-        mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
+        if constexpr (WIDE) {
+          uint4 vr[D / 32];
+          #pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+            vr[b] = *reinterpret_cast<const uint4 *>(pg + L::KBYTES + vw + b * 32 * (kBlock * 2));
+          mfma_page_wide<D>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
+        } else {
+          uint2 vr[ND];
+          #pragma unroll
+          for (int t = 0; t < ND; ++t)
+            vr[t] = *reinterpret_cast<const uint2 *>(pg + L::KBYTES + vb + t * 16 * (kBlock * 2));
+          mfma_page<D, NT>(a, si, (j0 + p) * kBlock, kr, vr, ((ok_bits >> p) & 1) != 0, lane, w, st);
+        }
       }
     }
   };

@@ -24,6 +24,10 @@
 
 namespace pkv {
 
+#ifndef PKV_PREFILL_WIDE
+#define PKV_PREFILL_WIDE 1
+#endif
+
 constexpr int kPrefillNT = 2;                    // 16-row MFMA tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 
@@ -38,6 +42,7 @@ constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 //    fits three waves per SIMD.
 template <int D, bool F8> struct PrefillCfg {
   static constexpr bool DMA = !F8 && D == 128;
+  static constexpr bool WIDE = DMA && PKV_PREFILL_WIDE;   // value products at the full rate
   static constexpr int SP = DMA ? 3 : F8 ? 2 : 4;
   static constexpr int WAVES_PER_SIMD = DMA || F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
 };
@@ -116,19 +121,24 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
 
   WaveRows<D, NT> w;
   load_rows<D, NT>(a, si, kvh, row0, rows, col, grp, w);
-  WaveAcc<D, NT> st;
-  init_acc<D, NT>(st);
+  typename std::conditional<Cfg::WIDE, WaveAccWide<D>, WaveAcc<D, NT>>::type st;
+  if constexpr (Cfg::WIDE) init_acc<D>(st);
+  else init_acc<D, NT>(st);
 
   const int32_t *bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   if constexpr (Cfg::DMA) {
     __shared__ __attribute__((aligned(16))) char buf0[DmaPages<SP>::BYTES];
     __shared__ __attribute__((aligned(16))) char buf1[DmaPages<SP>::BYTES];
-    lds_stream_pages_dma<NT, SP>(a, si, kvh, bt, 0, npages, my_pages, buf0, buf1, w, st);
-  } else {
+    lds_stream_pages_dma<NT, SP, Cfg::WIDE>(a, si, kvh, bt, 0, npages, my_pages, buf0, buf1, w, st);
+  } else if constexpr (!Cfg::WIDE) {
     __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
     lds_stream_pages<D, NT, SP, F8>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
   }
-  if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
+  if constexpr (Cfg::WIDE) {
+    if (row0 < rows) finish_wave_wide<D>(a, lane, w, st);
+  } else {
+    if (row0 < rows) finish_wave<D, NT>(a, 0, true, lane, w, st);
+  }
 }
 
 // f8: E4M3 pools (pages widened to bf16 as they are staged).
