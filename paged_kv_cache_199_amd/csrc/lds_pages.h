@@ -23,124 +23,6 @@ namespace pkv {
 
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
 
-template <int D, int SP>
-struct LdsPages {
-  static constexpr int ROWB = D * 2;
-  static constexpr int KPAD = ROWB + PKV_LDS_KPAD;   // LDS row stride of a K page
-  static constexpr int KBYTES = kBlock * KPAD;
-  static constexpr int VROW = kBlock * 2;            // LDS stride of a V dim row (16 tokens)
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int PBYTES = KBYTES + VBYTES;
-  static constexpr int CH = ROWB / 16;               // 16-byte chunks per K row
-  static constexpr int BYTES = 2 * SP * PBYTES;
-};
-
-// Logical pages [jb, je) of block-table row bt (kv head kvh) through LDS buffer `lds`
-// (LdsPages<D, SP>::BYTES).  Every thread of the workgroup must call it (it holds barriers); this
-// wave computes the pages j < jw with its rows (jw <= je; a wave with no rows passes jw = jb).
-// F8: the pools hold E4M3 codes; each 16-code chunk is widened exactly to bf16 as it is staged, so
-// LDS and everything after it are as for bf16 pools (the pools' scales sit in the score scale and
-// the epilogue).
-template <int D, int NT, int SP, bool F8 = false>
-__device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
-                                                 const int32_t *bt, int jb, int je, int jw, char *lds,
-                                                 const WaveRows<D, NT> &w, WaveAcc<D, NT> &st) {
-  typedef LdsPages<D, SP> L;
-  constexpr int NK = D / 32;
-  constexpr int ND = D / 16;
-  constexpr int EB = F8 ? 1 : 2;               // bytes per cache element
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int n = je - jb;
-  if (n <= 0) return;
-  const int nstages = (n + SP - 1) / SP;
-  const char *kbase = static_cast<const char *>(a.k_cache);
-  const char *vbase = static_cast<const char *>(a.v_cache);
-  const int64_t page_bytes = (int64_t)kBlock * D * EB;
-  // each thread moves 8 elements of every K page and 8 of every V page (a 16-byte chunk of bf16, or
-  // 8 bytes of codes); D = 64: threads < 128
-  typedef typename std::conditional<F8, uint2, uint4>::type Chunk;
-  const bool mover = tid < kBlock * D / 8;
-  Chunk kn[SP], vn[SP];
-  int okn = 0;                               // bit p: page p of the stage has a valid id
-  auto fetch = [&](int stage) {
-    okn = 0;
-    #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      const int j = jb + min(stage * SP + p, n - 1);   // past the end: re-read the last page
-      const int bid = bt[j];
-      const bool ok = bid >= 0 && bid < a.num_blocks;
-      okn |= ok ? 1 << p : 0;
-      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * (int)sizeof(Chunk);
-      if (mover) {
-        kn[p] = *reinterpret_cast<const Chunk *>(kbase + off);
-        vn[p] = *reinterpret_cast<const Chunk *>(vbase + off);
-      }
-    }
-  };
-  auto stage_to = [&](int b) {
-    if (mover) {
-      #pragma unroll
-      for (int p = 0; p < SP; ++p) {
-        char *pg = lds + (b * SP + p) * L::PBYTES;
-        // widened to 8 bf16 (F8: exact), the thread's elements are in the bf16 page's order
-        uint4 k8, v8;
-        if constexpr (F8) {
-          k8 = make_uint4(fp8x2_to_bf16x2<false>(kn[p].x), fp8x2_to_bf16x2<true>(kn[p].x),
-                          fp8x2_to_bf16x2<false>(kn[p].y), fp8x2_to_bf16x2<true>(kn[p].y));
-          v8 = make_uint4(fp8x2_to_bf16x2<false>(vn[p].x), fp8x2_to_bf16x2<true>(vn[p].x),
-                          fp8x2_to_bf16x2<false>(vn[p].y), fp8x2_to_bf16x2<true>(vn[p].y));
-        } else {
-          k8 = kn[p];
-          v8 = vn[p];
-        }
-        // K: elements 8 tid .. +7 are dims (8 tid) % D .. +7 of token 8 tid / D
-        *reinterpret_cast<uint4 *>(pg + (tid / L::CH) * L::KPAD + (tid % L::CH) * 16) = k8;
-        // V: elements 8 tid .. +7 are tokens 8 (tid & 1) .. +7 of dim tid / 2, i.e. its 4-token groups
-        // 2 (tid & 1) and 2 (tid & 1) + 1, stored in slots group ^ vswz(dim)
-        const int d = tid >> 1;
-        const int g0 = ((tid & 1) * 2) ^ vswz(d);
-        char *vrow = pg + L::KBYTES + d * L::VROW;
-        *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(v8.x, v8.y);
-        *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(v8.z, v8.w);
-      }
-    }
-  };
-
-  fetch(0);
-  stage_to(0);
-  int ok_cur = __builtin_amdgcn_readfirstlane(okn);
-  __syncthreads();
-  for (int g = 0; g < nstages; ++g) {
-    const int b = g & 1;
-    if (g + 1 < nstages) fetch(g + 1);
-    #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      const int j = jb + g * SP + p;
-      if (j < jw) {
-        const char *pg = lds + (b * SP + p) * L::PBYTES;
-        uint4 kr[NK];
-        uint2 vr[ND];
-        const char *kl = pg + col * L::KPAD + grp * 16;
-        #pragma unroll
-        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
-        const char *vl = pg + L::KBYTES + col * L::VROW;
-        #pragma unroll
-        for (int t = 0; t < ND; ++t)
-          vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * L::VROW + (grp ^ vswz(col + 16 * t)) * 8);
-        mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
-      }
-    }
-    if (g + 1 < nstages) {
-      stage_to(b ^ 1);
-      ok_cur = __builtin_amdgcn_readfirstlane(okn);
-    }
-    __syncthreads();
-  }
-}
-
 // ---- Value products at the full matrix-core rate (two 16-row tiles per wave, D = 128) ----
 // A 16-token page gives the P.V product only 16 keys, so v_mfma_f32_16x16x16_bf16 runs it at half
 // the matrix cores' rate (16 of the page step's 24 matrix-core instructions).  v_mfma_f32_32x32x16_bf16
@@ -299,6 +181,139 @@ __device__ __forceinline__ void finish_wave_wide(const DecodeArgs &a, int lane, 
     }
   }
   if (lane < 32 && a.lse) a.lse[orow] = lse2 * kLn2;
+}
+
+template <int D, int SP>
+struct LdsPages {
+  static constexpr int ROWB = D * 2;
+  static constexpr int KPAD = ROWB + PKV_LDS_KPAD;   // LDS row stride of a K page
+  static constexpr int KBYTES = kBlock * KPAD;
+  static constexpr int VROW = kBlock * 2;            // LDS stride of a V dim row (16 tokens)
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int PBYTES = KBYTES + VBYTES;
+  static constexpr int CH = ROWB / 16;               // 16-byte chunks per K row
+  static constexpr int BYTES = 2 * SP * PBYTES;
+};
+
+// Logical pages [jb, je) of block-table row bt (kv head kvh) through LDS buffer `lds`
+// (LdsPages<D, SP>::BYTES).  Every thread of the workgroup must call it (it holds barriers); this
+// wave computes the pages j < jw with its rows (jw <= je; a wave with no rows passes jw = jb).
+// F8: the pools hold E4M3 codes; each 16-code chunk is widened exactly to bf16 as it is staged, so
+// LDS and everything after it are as for bf16 pools (the pools' scales sit in the score scale and
+// the epilogue).
+// WIDE: the value products at the full rate (mfma_page_wide; st a WaveAccWide, NT = 2), with each V
+// dim row's two 8-token halves swapped where bit 3 of the dim is set.
+template <int D, int NT, int SP, bool F8 = false, bool WIDE = false, class ST>
+__device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqInfo &si, int kvh,
+                                                 const int32_t *bt, int jb, int je, int jw, char *lds,
+                                                 const WaveRows<D, NT> &w, ST &st) {
+  typedef LdsPages<D, SP> L;
+  constexpr int NK = D / 32;
+  constexpr int ND = D / 16;
+  constexpr int EB = F8 ? 1 : 2;               // bytes per cache element
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int n = je - jb;
+  if (n <= 0) return;
+  const int nstages = (n + SP - 1) / SP;
+  const char *kbase = static_cast<const char *>(a.k_cache);
+  const char *vbase = static_cast<const char *>(a.v_cache);
+  const int64_t page_bytes = (int64_t)kBlock * D * EB;
+  // each thread moves 8 elements of every K page and 8 of every V page (a 16-byte chunk of bf16, or
+  // 8 bytes of codes); D = 64: threads < 128
+  typedef typename std::conditional<F8, uint2, uint4>::type Chunk;
+  const bool mover = tid < kBlock * D / 8;
+  Chunk kn[SP], vn[SP];
+  int okn = 0;                               // bit p: page p of the stage has a valid id
+  auto fetch = [&](int stage) {
+    okn = 0;
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = jb + min(stage * SP + p, n - 1);   // past the end: re-read the last page
+      const int bid = bt[j];
+      const bool ok = bid >= 0 && bid < a.num_blocks;
+      okn |= ok ? 1 << p : 0;
+      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * (int)sizeof(Chunk);
+      if (mover) {
+        kn[p] = *reinterpret_cast<const Chunk *>(kbase + off);
+        vn[p] = *reinterpret_cast<const Chunk *>(vbase + off);
+      }
+    }
+  };
+  auto stage_to = [&](int b) {
+    if (mover) {
+      #pragma unroll
+      for (int p = 0; p < SP; ++p) {
+        char *pg = lds + (b * SP + p) * L::PBYTES;
+        // widened to 8 bf16 (F8: exact), the thread's elements are in the bf16 page's order
+        uint4 k8, v8;
+        if constexpr (F8) {
+          k8 = make_uint4(fp8x2_to_bf16x2<false>(kn[p].x), fp8x2_to_bf16x2<true>(kn[p].x),
+                          fp8x2_to_bf16x2<false>(kn[p].y), fp8x2_to_bf16x2<true>(kn[p].y));
+          v8 = make_uint4(fp8x2_to_bf16x2<false>(vn[p].x), fp8x2_to_bf16x2<true>(vn[p].x),
+                          fp8x2_to_bf16x2<false>(vn[p].y), fp8x2_to_bf16x2<true>(vn[p].y));
+        } else {
+          k8 = kn[p];
+          v8 = vn[p];
+        }
+        // K: elements 8 tid .. +7 are dims (8 tid) % D .. +7 of token 8 tid / D
+        *reinterpret_cast<uint4 *>(pg + (tid / L::CH) * L::KPAD + (tid % L::CH) * 16) = k8;
+        // V: elements 8 tid .. +7 are tokens 8 (tid & 1) .. +7 of dim tid / 2, i.e. its 4-token groups
+        // 2 (tid & 1) and 2 (tid & 1) + 1, stored in slots group ^ vswz(dim)
+        const int d = tid >> 1;
+        char *vrow = pg + L::KBYTES + d * L::VROW;
+        if constexpr (WIDE) {
+          *reinterpret_cast<uint4 *>(vrow + (((tid & 1) ^ ((d >> 3) & 1)) * 16)) = v8;
+        } else {
+          const int g0 = ((tid & 1) * 2) ^ vswz(d);
+          *reinterpret_cast<uint2 *>(vrow + g0 * 8) = make_uint2(v8.x, v8.y);
+          *reinterpret_cast<uint2 *>(vrow + (g0 ^ 1) * 8) = make_uint2(v8.z, v8.w);
+        }
+      }
+    }
+  };
+
+  fetch(0);
+  stage_to(0);
+  int ok_cur = __builtin_amdgcn_readfirstlane(okn);
+  __syncthreads();
+  for (int g = 0; g < nstages; ++g) {
+    const int b = g & 1;
+    if (g + 1 < nstages) fetch(g + 1);
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int j = jb + g * SP + p;
+      if (j < jw) {
+        const char *pg = lds + (b * SP + p) * L::PBYTES;
+        uint4 kr[NK];
+        const char *kl = pg + col * L::KPAD + grp * 16;
+        #pragma unroll
+        for (int c = 0; c < NK; ++c) kr[c] = *reinterpret_cast<const uint4 *>(kl + c * 64);
+        if constexpr (WIDE) {
+          // dim l % 32 of each 32-dim block, tokens 8 (l / 32) .. + 7
+          const char *vl = pg + L::KBYTES + (lane & 31) * L::VROW + (((lane >> 5) ^ ((lane >> 3) & 1)) * 16);
+          uint4 vr[D / 32];
+          #pragma unroll
+          for (int bk = 0; bk < D / 32; ++bk) vr[bk] = *reinterpret_cast<const uint4 *>(vl + bk * 32 * L::VROW);
+          mfma_page_wide<D>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
+        } else {
+          uint2 vr[ND];
+          const char *vl = pg + L::KBYTES + col * L::VROW;
+          #pragma unroll
+          for (int t = 0; t < ND; ++t)
+            vr[t] = *reinterpret_cast<const uint2 *>(vl + t * 16 * L::VROW + (grp ^ vswz(col + 16 * t)) * 8);
+          mfma_page<D, NT>(a, si, j * kBlock, kr, vr, ((ok_cur >> p) & 1) != 0, lane, w, st);
+        }
+      }
+    }
+    if (g + 1 < nstages) {
+      stage_to(b ^ 1);
+      ok_cur = __builtin_amdgcn_readfirstlane(okn);
+    }
+    __syncthreads();
+  }
 }
 
 // bf16 pools, D = 128: the same page walk with each stage fetched by gfx950's global-to-LDS loads

@@ -42,7 +42,7 @@ constexpr int kPrefillRows = 4 * 16 * kPrefillNT;   // rows per workgroup
 //    fits three waves per SIMD.
 template <int D, bool F8> struct PrefillCfg {
   static constexpr bool DMA = !F8 && D == 128;
-  static constexpr bool WIDE = DMA && PKV_PREFILL_WIDE;   // value products at the full rate
+  static constexpr bool WIDE = PKV_PREFILL_WIDE;   // value products at the full rate
   static constexpr int SP = DMA ? 3 : F8 ? 2 : 4;
   static constexpr int WAVES_PER_SIMD = DMA || F8 ? 3 : 1;   // 1: no limit beyond the workgroup size
 };
@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
     __shared__ __attribute__((aligned(16))) char buf0[DmaPages<SP>::BYTES];
     __shared__ __attribute__((aligned(16))) char buf1[DmaPages<SP>::BYTES];
     lds_stream_pages_dma<NT, SP, Cfg::WIDE>(a, si, kvh, bt, 0, npages, my_pages, buf0, buf1, w, st);
-  } else if constexpr (!Cfg::WIDE) {
+  } else {
     __shared__ __attribute__((aligned(16))) char lds[LdsPages<D, SP>::BYTES];
-    lds_stream_pages<D, NT, SP, F8>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
+    lds_stream_pages<D, NT, SP, F8, Cfg::WIDE>(a, si, kvh, bt, 0, npages, my_pages, lds, w, st);
   }
   if constexpr (Cfg::WIDE) {
     if (row0 < rows) finish_wave_wide<D>(a, lane, w, st);
