@@ -23,7 +23,7 @@ namespace pkv {
 
 __device__ __forceinline__ int vswz(int d) { return (d >> 2) & 3; }
 
-// ---- Value products at the full matrix-core rate (two 16-row tiles per wave, D = 128) ----
+// ---- Value products at the full matrix-core rate (two 16-row tiles per wave, D = 64 or 128) ----
 // A 16-token page gives the P.V product only 16 keys, so v_mfma_f32_16x16x16_bf16 runs it at half
 // the matrix cores' rate (16 of the page step's 24 matrix-core instructions).  v_mfma_f32_32x32x16_bf16
 // takes the same 16 keys at the full rate: O^T[d][r] += sum_t V^T[d][t] P^T[t][r] for 32 dims x 32
