@@ -118,11 +118,14 @@ __global__ __launch_bounds__(256, (PrefillCfg<D, F8>::WAVES_PER_SIMD)) void pref
   const int row0 = wg_row0 + wave * WROWS;
   // the pages this workgroup reads: up to its last row's last visible key
   const int wg_last_tok = (min(rows, wg_row0 + kPrefillRows) - 1) / G;
-  const int npages = (si.ctx - si.qs + wg_last_tok) / kBlock + 1;
-  const int my_pages = row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + WROWS) - 1) / G) / kBlock + 1 : 0;
+  // wave-uniform bounds held in scalar registers, so the per-page tests against them are scalar
+  const int npages = __builtin_amdgcn_readfirstlane((si.ctx - si.qs + wg_last_tok) / kBlock + 1);
+  const int my_pages = __builtin_amdgcn_readfirstlane(
+      row0 < rows ? (si.ctx - si.qs + (min(rows, row0 + WROWS) - 1) / G) / kBlock + 1 : 0);
 
   WaveRows<D, NT> w;
   load_rows<D, NT>(a, si, kvh, row0, rows, col, grp, w);
+  w.first_last = __builtin_amdgcn_readfirstlane(w.first_last);
   typename std::conditional<Cfg::WIDE, WaveAccWide<D>, WaveAcc<D, NT>>::type st;
   if constexpr (Cfg::WIDE) init_acc<D>(st);
   else init_acc<D, NT>(st);
