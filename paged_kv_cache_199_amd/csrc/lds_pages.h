@@ -373,19 +373,31 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   };
   // issue the loads of the stage whose ids are in idv into buffer dst; returns bit p set when page p
   // has a valid block id
+  // the page test, addresses and LDS targets are wave-uniform: kept in scalar registers, with the
+  // lane's part as a 32-bit offset (a block id is an int, so comparing it with the pool size clamped
+  // to int range is exact)
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)0x7fffffff);
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t k_off32 = (uint32_t)k_off, v_off32 = (uint32_t)v_off;
   auto fetch = [&](char *dst) -> int {
     int okn = 0;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
       const int bid = __builtin_amdgcn_readlane(idv, p);
-      const bool ok = bid >= 0 && bid < a.num_blocks;
+      const bool ok = (uint32_t)bid < nb32;
       okn |= ok ? 1 << p : 0;
       const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
+      const char *kp = kbase + page;
+      const char *vp = vbase + page;
       char *pg = dst + p * L::PBYTES;
-      __builtin_amdgcn_global_load_lds(kbase + page + k_off, (__attribute__((address_space(3))) void *)(pg + wave * 1024),
+      // opaque here, so the 32-bit offsets are not widened and hoisted, and the loads take the scalar
+      // base plus a 32-bit lane offset
+      uint32_t ko = k_off32, vo = v_off32;
+      asm volatile("" : "+v"(ko), "+v"(vo));
+      __builtin_amdgcn_global_load_lds(kp + ko, (__attribute__((address_space(3))) void *)(pg + swave * 1024),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + page + v_off,
-                                       (__attribute__((address_space(3))) void *)(pg + L::KBYTES + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + vo,
+                                       (__attribute__((address_space(3))) void *)(pg + L::KBYTES + swave * 1024), 16, 0, 0);
     }
     return okn;
   };
