@@ -227,18 +227,29 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
   const bool mover = tid < kBlock * D / 8;
   Chunk kn[SP], vn[SP];
   int okn = 0;                               // bit p: page p of the stage has a valid id
-  auto fetch = [&](int stage) {
+  // block ids through the scalar cache, read a stage before they are used; the page test and page
+  // bases stay in scalar registers and each load takes a scalar base plus the thread's 32-bit offset
+  // (a block id is an int, so comparing it with the pool size clamped to int range is exact)
+  const_i32 *btc = (const_i32 *)(bt + jb);
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)0x7fffffff);
+  int nid[SP];
+  auto load_ids = [&](int stage) {
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) nid[p] = btc[__builtin_amdgcn_readfirstlane(min(stage * SP + p, n - 1))];
+  };
+  auto fetch = [&]() {   // the stage whose ids are in nid; past the end the last page again
     okn = 0;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      const int j = jb + min(stage * SP + p, n - 1);   // past the end: re-read the last page
-      const int bid = bt[j];
-      const bool ok = bid >= 0 && bid < a.num_blocks;
+      const int bid = nid[p];
+      const bool ok = (uint32_t)bid < nb32;
       okn |= ok ? 1 << p : 0;
-      const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes + tid * (int)sizeof(Chunk);
+      const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
       if (mover) {
-        kn[p] = *reinterpret_cast<const Chunk *>(kbase + off);
-        vn[p] = *reinterpret_cast<const Chunk *>(vbase + off);
+        uint32_t to = (uint32_t)tid * (uint32_t)sizeof(Chunk);
+        asm volatile("" : "+v"(to));   // keeps the offset 32-bit, so the loads use the scalar base
+        kn[p] = *reinterpret_cast<const Chunk *>(kbase + page + to);
+        vn[p] = *reinterpret_cast<const Chunk *>(vbase + page + to);
       }
     }
   };
@@ -275,13 +286,18 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
     }
   };
 
-  fetch(0);
+  load_ids(0);
+  fetch();
+  load_ids(1);
   stage_to(0);
   int ok_cur = __builtin_amdgcn_readfirstlane(okn);
   __syncthreads();
   for (int g = 0; g < nstages; ++g) {
     const int b = g & 1;
-    if (g + 1 < nstages) fetch(g + 1);
+    if (g + 1 < nstages) {
+      fetch();
+      load_ids(g + 2);
+    }
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
       const int j = jb + g * SP + p;
