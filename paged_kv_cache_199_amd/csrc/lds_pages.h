@@ -380,14 +380,15 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const int k_off = (4 * wave + (lane & 3)) * (D * 2) + (4 * (lane >> 4) + k_slot_g) * 16;
   const int vd = 32 * wave + (lane >> 1);
   const int v_off = vd * (kBlock * 2) + (((lane & 1) ^ ((vd >> (WIDE ? 3 : 2)) & 1)) * 16);
-  // block ids of the next stage to fetch (lane p: page p), read one stage ahead and issued after a
-  // stage's global-to-LDS loads, so the stage-end wait covers both and no fetch waits for an id (read
-  // when needed, the id's wait would also count the loads in flight)
-  int idv = 0;
+  // block ids of the next stage to fetch, read one stage ahead through the scalar cache (their wait
+  // counts no vector loads, and it comes after the stage-end barrier, with no LDS read in flight)
+  const_i32 *btc = (const_i32 *)(bt + jb);
+  int nid[SP];
   auto ids_of = [&](int g) {
-    idv = bt[jb + min(g * SP + min(lane, SP - 1), n - 1)];   // past the end: the last page
+    #pragma unroll
+    for (int p = 0; p < SP; ++p) nid[p] = btc[__builtin_amdgcn_readfirstlane(min(g * SP + p, n - 1))];
   };
-  // issue the loads of the stage whose ids are in idv into buffer dst; returns bit p set when page p
+  // issue the loads of the stage whose ids are in nid into buffer dst; returns bit p set when page p
   // has a valid block id
   // the page test, addresses and LDS targets are wave-uniform: kept in scalar registers, with the
   // lane's part as a 32-bit offset (a block id is an int, so comparing it with the pool size clamped
@@ -399,7 +400,7 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
     int okn = 0;
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
-      const int bid = __builtin_amdgcn_readlane(idv, p);
+      const int bid = nid[p];
       const bool ok = (uint32_t)bid < nb32;
       okn |= ok ? 1 << p : 0;
       const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
