@@ -398,19 +398,21 @@ __device__ __forceinline__ void lds_stream_pages_dma(const DecodeArgs &a, const 
   const uint32_t k_off32 = (uint32_t)k_off, v_off32 = (uint32_t)v_off;
   auto fetch = [&](char *dst) -> int {
     int okn = 0;
+    // opaque here, so the 32-bit offsets are not widened and hoisted, and the loads take the scalar
+    // page base plus a 32-bit lane offset
+    uint32_t ko = k_off32, vo = v_off32;
+    asm volatile("" : "+v"(ko), "+v"(vo));
     #pragma unroll
     for (int p = 0; p < SP; ++p) {
       const int bid = nid[p];
-      const bool ok = (uint32_t)bid < nb32;
-      okn |= ok ? 1 << p : 0;
-      const int64_t page = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * page_bytes;
+      // 1 when bid < nb32 as unsigned, in scalar arithmetic (the difference of two values below 2^32
+      // is negative exactly then)
+      const int okb = (int)((uint64_t)((int64_t)(uint32_t)bid - (int64_t)nb32) >> 63);
+      okn |= okb << p;
+      const int64_t page = ((int64_t)(bid & -okb) * a.num_kv_heads + kvh) * page_bytes;
       const char *kp = kbase + page;
       const char *vp = vbase + page;
       char *pg = dst + p * L::PBYTES;
-      // opaque here, so the 32-bit offsets are not widened and hoisted, and the loads take the scalar
-      // base plus a 32-bit lane offset
-      uint32_t ko = k_off32, vo = v_off32;
-      asm volatile("" : "+v"(ko), "+v"(vo));
       __builtin_amdgcn_global_load_lds(kp + ko, (__attribute__((address_space(3))) void *)(pg + swave * 1024),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds(vp + vo,
