@@ -183,6 +183,16 @@ __device__ __forceinline__ void finish_wave_wide(const DecodeArgs &a, int lane, 
   if (lane < 32 && a.lse) a.lse[orow] = lse2 * kLn2;
 }
 
+// Two E4M3 codes (the low or high half of w) to two bf16 in one instruction: gfx950's scaled
+// conversion straight to bf16, at scale 1.  Every E4M3 value is a bf16 value, so it is exact; an
+// in-bounds probe over all 256 codes in both halves matched the fp8 -> f32 conversion with its low
+// 16 bits dropped (fp8x2_to_bf16x2) bit for bit, NaN codes included.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2_1(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 template <int D, int SP>
 struct LdsPages {
   static constexpr int ROWB = D * 2;
@@ -261,10 +271,10 @@ __device__ __forceinline__ void lds_stream_pages(const DecodeArgs &a, const SeqI
         // widened to 8 bf16 (F8: exact), the thread's elements are in the bf16 page's order
         uint4 k8, v8;
         if constexpr (F8) {
-          k8 = make_uint4(fp8x2_to_bf16x2<false>(kn[p].x), fp8x2_to_bf16x2<true>(kn[p].x),
-                          fp8x2_to_bf16x2<false>(kn[p].y), fp8x2_to_bf16x2<true>(kn[p].y));
-          v8 = make_uint4(fp8x2_to_bf16x2<false>(vn[p].x), fp8x2_to_bf16x2<true>(vn[p].x),
-                          fp8x2_to_bf16x2<false>(vn[p].y), fp8x2_to_bf16x2<true>(vn[p].y));
+          k8 = make_uint4(fp8x2_to_bf16x2_1<false>(kn[p].x), fp8x2_to_bf16x2_1<true>(kn[p].x),
+                          fp8x2_to_bf16x2_1<false>(kn[p].y), fp8x2_to_bf16x2_1<true>(kn[p].y));
+          v8 = make_uint4(fp8x2_to_bf16x2_1<false>(vn[p].x), fp8x2_to_bf16x2_1<true>(vn[p].x),
+                          fp8x2_to_bf16x2_1<false>(vn[p].y), fp8x2_to_bf16x2_1<true>(vn[p].y));
         } else {
           k8 = kn[p];
           v8 = vn[p];
